@@ -1,0 +1,160 @@
+/*
+ * jetlong.h — C ABI of the MI355X (gfx950) dynamic bifocal RoPE attention
+ * library (libjetlong.so).
+ *
+ * The method: "Jet-Long: Efficient Long-Context Extension with Dynamic
+ * Bifocal RoPE" (gist.science technical summaries of arXiv 2607.07740).
+ *   - Section "Dynamic Bifocal RoPE": a causal query/key pair whose distance
+ *     is below the local window w0 is scored with classic RoPE at the true
+ *     positions; every farther pair is scored with RoPE at the grouped
+ *     positions f(x) = floor(x / G), G = max(1, ceil(L / w_pretrained)),
+ *     recomputed from the current sequence length L (eq. G, eq. f).
+ *   - Section "Inference Efficiency Mechanisms": the KV cache keeps the base
+ *     keys at their exact absolute positions and is never rewritten; the
+ *     rotation that the remote branch needs is applied on the fly.
+ *
+ * Readings taken where the pages are silent:
+ *   RoPE: theta_k = theta^(-2k/d), rotate-half pairing (dims k and k + d/2);
+ *   the remote branch rotates every token by f of its own absolute position
+ *   (no extra offset); the local window holds distances 0 .. w0-1 (w0 = 0
+ *   makes every pair remote); softmax scale 1/sqrt(d) unless given; GQA query
+ *   head h reads KV head h / (Hq / Hkv); in decode L counts the new token.
+ *
+ * Conventions shared by every entry point
+ *   Memory:   the caller allocates and frees every buffer (inputs, outputs,
+ *             workspace).  Pointers marked "device" must be device memory of
+ *             the current HIP device.  The library keeps no device state
+ *             between calls and allocates nothing.
+ *   Streams:  `stream` is a hipStream_t passed as void* (NULL = the default
+ *             stream).  Work is only enqueued; nothing synchronises the host.
+ *             The host never reads device arguments such as cu_seqlens.
+ *   Errors:   every argument is checked before any HIP call; on failure the
+ *             call returns a negative jl_status, enqueues nothing and records
+ *             a message for jl_last_error().  A launch failure returns
+ *             JL_ERR_HIP.  A device fault surfaces at the caller's next
+ *             synchronisation.  No C++ exception crosses this interface.
+ *   dtype:    JL_F32 (float) or JL_BF16 (bfloat16, round-to-nearest-even on
+ *             output).  Accumulation, softmax and rotation run in fp32; the
+ *             RoPE angles and their cos/sin are formed in fp64.
+ *   head_dim: 64 or 128.  Hq must be a multiple of Hkv.
+ *   Limits:   sequence lengths < 2^31; positions are int32.
+ */
+#ifndef JETLONG_H
+#define JETLONG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JL_OK = 0,
+  JL_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % Hkv != 0 ... */
+  JL_ERR_UNSUPPORTED = -2, /* head_dim or dtype outside the supported set   */
+  JL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required    */
+  JL_ERR_HIP = -4          /* a HIP call failed (launch, device query)      */
+} jl_status;
+
+typedef enum { JL_F32 = 0, JL_BF16 = 1 } jl_dtype;
+
+/* Tile class codes of jl_bifocal_tile_classes (low two bits) and the flag
+ * bit for a tile that also holds pairs with the key after the query. */
+enum { JL_TILE_SKIP = 0, JL_TILE_LOCAL = 1, JL_TILE_REMOTE = 2, JL_TILE_STRADDLE = 3,
+       JL_TILE_DIAG = 4 };
+
+/* Group size G = max(1, ceil(L / w_pretrained)) in exact integer arithmetic
+ * ("Dynamic Bifocal RoPE", eq. G).  Host only.  Returns G >= 1, or
+ * JL_ERR_INVALID_ARG when L < 0 or w_pretrained < 1. */
+int64_t jl_bifocal_group_size(int64_t L, int64_t w_pretrained);
+
+/* Bytes of device workspace jl_bifocal_prefill needs for these sizes, or 0 on
+ * invalid sizes.  total_k = number of packed key rows (cu_seqlens_k[B]). */
+size_t jl_bifocal_prefill_workspace_size(int dtype, int B, int total_k, int max_seqlen_k,
+                                         int Hq, int Hkv, int head_dim);
+
+/* Packed variable-length causal prefill ("Dynamic Bifocal RoPE"; the
+ * "Inclusion-Exclusion Attention Merge" of the pages reaches the same result
+ * by three merged passes; this library routes each key tile instead).
+ *
+ *   q   device [total_q, Hq, head_dim]   dtype   raw (un-rotated) queries
+ *   k,v device [total_k, Hkv, head_dim]  dtype   raw keys / values, read only
+ *   o   device [total_q, Hq, head_dim]   dtype   output
+ *   lse device [Hq, total_q] float or NULL: natural-log log-sum-exp per row
+ *   cu_seqlens_q device int32 [B+1]: sequence b owns query rows
+ *       cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *   cu_seqlens_k device int32 [B+1] or NULL (= cu_seqlens_q).  Sequence b
+ *       has L_b = cu_seqlens_k[b+1]-cu_seqlens_k[b] keys at positions
+ *       0 .. L_b-1 and its Lq_b queries sit at the last Lq_b positions
+ *       (L_b - Lq_b .. L_b - 1; a chunk of a longer prefill); Lq_b <= L_b is
+ *       required.  G_b is computed from L_b on the device.
+ *   max_seqlen_q / max_seqlen_k: upper bounds of Lq_b / L_b.
+ *   w_pretrained >= 1, w0 >= 0, rope_theta > 0.
+ *   softmax_scale: 0 selects 1/sqrt(head_dim).
+ *   workspace: device, >= jl_bifocal_prefill_workspace_size(...) bytes,
+ *       256-byte aligned; contents need not be initialised.
+ */
+int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                       int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                       double rope_theta, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace jl_bifocal_decode needs, or 0 on invalid sizes. */
+size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv,
+                                        int head_dim);
+
+/* One new query per sequence against an untouched KV cache ("Inference
+ * Efficiency Mechanisms": base keys stay at their absolute positions; the
+ * rotation each key needs is applied in registers, the cache is never
+ * written).
+ *
+ *   q   device [B, Hq, head_dim] dtype, raw query of the newest token
+ *   k_cache, v_cache device, dtype, raw keys/values; element (b, s, h, e) at
+ *       offset b*stride_b + s*stride_s + h*stride_h + e (strides in elements,
+ *       head_dim contiguous, same strides for both caches).  Read only.
+ *   o   device [B, Hq, head_dim] dtype output; lse device [B, Hq] float or NULL
+ *   seq_L device int32 [B]: keys valid in sequence b, the new token included
+ *       (1 <= seq_L[b] <= max_L); the query sits at position seq_L[b]-1.
+ *   workspace: device, >= jl_bifocal_decode_workspace_size(...) bytes.
+ */
+int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache,
+                      int64_t stride_b, int64_t stride_s, int64_t stride_h,
+                      void* o, float* lse, int dtype, const int32_t* seq_L, int B, int max_L,
+                      int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                      double rope_theta, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Integer position map of a packed batch, exactly as the prefill kernels use
+ * it (eq. G, eq. f).  Device outputs: pos_out/f_out int32 [total_q] (query
+ * position and its remote position), G_out int32 [B].  cu_seqlens_k may be
+ * NULL (= cu_seqlens_q). */
+int jl_bifocal_remote_positions(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int total_q, int w_pretrained, int32_t* pos_out, int32_t* f_out,
+                                int32_t* G_out, void* stream);
+
+/* Tile classes the prefill kernels use, for one sequence of Lq queries at
+ * positions L-Lq .. L-1 against L keys, in BM x BN blocks (1 <= BM, BN <=
+ * 4096).  cls_out: device uint8 [ceil(Lq/BM), ceil(L/BN)], row-major. */
+int jl_bifocal_tile_classes(int Lq, int L, int w0, int BM, int BN, uint8_t* cls_out,
+                            void* stream);
+
+/* Query-block height and key-tile width the bf16 prefill kernel routes on,
+ * for a given GQA ratio Hq/Hkv (so tests can compare its tile map). */
+int jl_bifocal_prefill_tile_shape(int dtype, int Hq, int Hkv, int head_dim, int* BM, int* BN);
+
+/* Static description of a status code. */
+const char* jl_status_string(int code);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* jl_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* jl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JETLONG_H */

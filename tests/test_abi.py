@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import zero_shot_rope_bifocal_amd as jl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jetlong.h")
+
+
+def _lib():
+    if not os.path.exists(jl.library_path()):
+        pytest.skip("libjetlong.so not built (run __graft_entry__.build())")
+    return jl.lib()
+
+
+def test_header_symbols_exported():
+    L = _lib()
+    names = re.findall(r"\b(jl_[a-z_0-9]+)\s*\(", open(HEADER).read())
+    assert len(set(names)) >= 11
+    for n in set(names):
+        assert hasattr(L, n), f"{n} declared in jetlong.h but not exported"
+
+
+def test_group_size_matches_golden():
+    _lib()
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "group_size.json")))
+    for c in g["group_size"]:
+        assert jl.group_size(c["L"], c["w_pretrained"]) == c["G"]
+    with pytest.raises(jl.JetLongError):
+        jl.group_size(5, 0)
+    with pytest.raises(jl.JetLongError):
+        jl.group_size(-1, 4)
+
+
+def _prefill(L, **kw):
+    a = dict(q=1, k=1, v=1, o=1, lse=None, dtype=jl.JL_BF16, cu_q=1, cu_k=None, B=1, total_q=64,
+             total_k=64, max_q=64, max_k=64, Hq=8, Hkv=2, d=128, wp=32, w0=4, theta=1e4, scale=0.0,
+             ws=256, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return L.jl_bifocal_prefill(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), a["dtype"],
+                                vp(a["cu_q"]), vp(a["cu_k"]), a["B"], a["total_q"], a["total_k"],
+                                a["max_q"], a["max_k"], a["Hq"], a["Hkv"], a["d"], a["wp"], a["w0"],
+                                a["theta"], a["scale"], vp(a["ws"]), a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -2), (dict(d=96), -2), (dict(Hq=6, Hkv=4), -1), (dict(Hkv=0), -1),
+    (dict(wp=0), -1), (dict(w0=-1), -1), (dict(theta=0.0), -1), (dict(theta=float("nan")), -1),
+    (dict(scale=-1.0), -1), (dict(q=None), -1), (dict(cu_q=None), -1), (dict(total_q=65), -1),
+    (dict(max_q=65), -1), (dict(ws=None), -3), (dict(ws_bytes=16), -3), (dict(ws=257), -3),
+    (dict(B=-1), -1), (dict(total_k=80), -1),
+])
+def test_prefill_rejects_before_any_launch(kw, code):
+    L = _lib()
+    assert _prefill(L, **kw) == code
+    assert L.jl_last_error().decode() != ""
+
+
+def test_prefill_empty_batch_is_ok():
+    L = _lib()
+    assert _prefill(L, B=0, q=None, k=None, v=None, o=None, cu_q=None, ws=None) == 0
+    assert _prefill(L, total_q=0, total_k=0, q=None, ws=None) == 0
+
+
+def _decode(L, **kw):
+    a = dict(q=256, kc=256, vc=256, sb=1 << 20, ss=1024, sh=128, o=1, lse=None, dtype=jl.JL_BF16,
+             seq_L=1, B=2, max_L=64, Hq=8, Hkv=2, d=128, wp=32, w0=4, theta=1e4, scale=0.0, ws=256,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return L.jl_bifocal_decode(vp(a["q"]), vp(a["kc"]), vp(a["vc"]), a["sb"], a["ss"], a["sh"], vp(a["o"]),
+                               vp(a["lse"]), a["dtype"], vp(a["seq_L"]), a["B"], a["max_L"], a["Hq"],
+                               a["Hkv"], a["d"], a["wp"], a["w0"], a["theta"], a["scale"], vp(a["ws"]),
+                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -2), (dict(d=32), -2), (dict(Hq=64, Hkv=2), -2), (dict(Hq=9), -1),
+    (dict(seq_L=None), -1), (dict(max_L=0), -1), (dict(ss=64), -1), (dict(sh=100), -1),
+    (dict(kc=258), -1), (dict(ws=None), -3), (dict(ws_bytes=1), -3), (dict(wp=0), -1),
+])
+def test_decode_rejects_before_any_launch(kw, code):
+    L = _lib()
+    assert _decode(L, **kw) == code
+
+
+def test_workspace_sizes():
+    _lib()
+    a = jl.prefill_workspace_size(jl.JL_BF16, 1, 131072, 131072, 32, 8, 128)
+    # cos/sin table + two rotated key copies + transposed values (padded rows)
+    assert a >= 131072 * 64 * 8 + 3 * 8 * 131072 * 128 * 2
+    assert jl.prefill_workspace_size(jl.JL_F32, 1, 2048, 2048, 2, 2, 64) >= 2048 * 32 * 8
+    assert jl.prefill_workspace_size(9, 1, 1, 1, 1, 1, 64) == 0
+    assert jl.decode_workspace_size(jl.JL_BF16, 16, 131072, 32, 8, 128) > 131072 * 64 * 8
+
+
+def test_tile_shape():
+    _lib()
+    assert jl.prefill_tile_shape(jl.JL_BF16, 32, 8, 128) == (64, 64)
+    assert jl.prefill_tile_shape(jl.JL_BF16, 8, 8, 128) == (256, 64)
+    assert jl.prefill_tile_shape(jl.JL_F32, 2, 2, 64) == (64, 32)
+
+
+def test_status_strings():
+    L = _lib()
+    for c in (0, -1, -2, -3, -4):
+        assert L.jl_status_string(c)
+    assert jl.version().count(".") == 2

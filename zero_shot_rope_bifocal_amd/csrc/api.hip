@@ -1,0 +1,206 @@
+// C ABI of libjetlong: argument validation and dispatch (include/jetlong.h).
+//
+// Every argument is checked before any HIP call; a failing call enqueues
+// nothing and leaves a message for jl_last_error() on the calling thread.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/jetlong.h"
+#include "jl_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return JL_OK;
+  return fail(JL_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool supported_dtype(int t) { return t == JL_F32 || t == JL_BF16; }
+
+int check_common(int dtype, int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                 double theta, float scale) {
+  if (!supported_dtype(dtype)) return fail(JL_ERR_UNSUPPORTED, "dtype %d not supported (JL_F32 or JL_BF16)", dtype);
+  if (!supported_dim(head_dim)) return fail(JL_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (Hq < 1 || Hkv < 1) return fail(JL_ERR_INVALID_ARG, "Hq=%d and Hkv=%d must be >= 1", Hq, Hkv);
+  if (Hq % Hkv) return fail(JL_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (w_pretrained < 1) return fail(JL_ERR_INVALID_ARG, "w_pretrained=%d must be >= 1", w_pretrained);
+  if (w0 < 0) return fail(JL_ERR_INVALID_ARG, "w0=%d must be >= 0", w0);
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(JL_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (!(scale >= 0.f) || !isfinite(scale)) return fail(JL_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  return JL_OK;
+}
+
+float resolve_scale(float scale, int head_dim) {
+  return scale == 0.f ? static_cast<float>(1.0 / sqrt(static_cast<double>(head_dim))) : scale;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t jl_bifocal_group_size(int64_t L, int64_t w_pretrained) {
+  if (L < 0 || w_pretrained < 1) {
+    fail(JL_ERR_INVALID_ARG, "group_size needs L >= 0 and w_pretrained >= 1");
+    return JL_ERR_INVALID_ARG;
+  }
+  const int64_t g = L / w_pretrained + (L % w_pretrained != 0);
+  return g < 1 ? 1 : g;
+}
+
+size_t jl_bifocal_prefill_workspace_size(int dtype, int B, int total_k, int max_seqlen_k, int Hq,
+                                         int Hkv, int head_dim) {
+  if (!supported_dtype(dtype) || !supported_dim(head_dim) || B < 0 || total_k < 0 ||
+      max_seqlen_k < 0 || Hq < 1 || Hkv < 1)
+    return 0;
+  if (dtype == JL_BF16) return jl::prefill_ws_bytes_bf16(B, total_k, max_seqlen_k, Hkv, head_dim);
+  return jl::prefill_ws_bytes_f32(max_seqlen_k, head_dim);
+}
+
+int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                       int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
+                       float softmax_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
+  if (st != JL_OK) return st;
+  if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
+  if (total_q > total_k) return fail(JL_ERR_INVALID_ARG, "total_q=%d exceeds total_k=%d", total_q, total_k);
+  if (max_seqlen_q > max_seqlen_k) return fail(JL_ERR_INVALID_ARG, "max_seqlen_q exceeds max_seqlen_k");
+  if (B == 0 || total_q == 0) return JL_OK;
+  if (!q || !k || !v || !o) return fail(JL_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  if (!cu_seqlens_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_q must be non-null");
+  if (!cu_seqlens_k && total_k != total_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_k is NULL but total_k != total_q");
+  if (max_seqlen_k < 1) return fail(JL_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 for a non-empty batch");
+  const size_t need = jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hq, Hkv, head_dim);
+  if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  jl::PrefillCall c{};
+  c.q = q; c.k = k; c.v = v; c.o = o; c.lse = lse;
+  c.cu_q = cu_seqlens_q;
+  c.cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
+  c.B = B; c.total_q = total_q; c.total_k = total_k;
+  c.max_q = max_seqlen_q; c.max_k = max_seqlen_k;
+  c.Hq = Hq; c.Hkv = Hkv; c.D = head_dim;
+  c.w_pretrained = w_pretrained; c.w0 = w0;
+  c.theta = rope_theta;
+  c.scale = resolve_scale(softmax_scale, head_dim);
+  c.ws = workspace;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16(c, s) : jl::launch_prefill_f32(c, s);
+  return hip_status(e, "jl_bifocal_prefill launch");
+}
+
+size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv, int head_dim) {
+  if (!supported_dtype(dtype) || !supported_dim(head_dim) || B < 0 || max_L < 0 || Hq < 1 || Hkv < 1)
+    return 0;
+  return jl::decode_ws_bytes(B, max_L, Hq, Hkv, head_dim);
+}
+
+int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
+                      int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
+                      const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
+                      int w_pretrained, int w0, double rope_theta, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
+  if (st != JL_OK) return st;
+  if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports up to 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (B < 0 || max_L < 0) return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
+  if (B == 0) return JL_OK;
+  if (max_L < 1) return fail(JL_ERR_INVALID_ARG, "max_L must be >= 1");
+  if (!q || !k_cache || !v_cache || !o || !seq_L) return fail(JL_ERR_INVALID_ARG, "q, caches, o and seq_L must be non-null");
+  if (stride_b < 0 || stride_s < head_dim || stride_h < head_dim)
+    return fail(JL_ERR_INVALID_ARG, "cache strides must be >= head_dim (got b=%lld s=%lld h=%lld)",
+                static_cast<long long>(stride_b), static_cast<long long>(stride_s), static_cast<long long>(stride_h));
+  if (dtype == JL_BF16 && (stride_b % 8 || stride_s % 8 || stride_h % 8))
+    return fail(JL_ERR_INVALID_ARG, "bf16 cache strides must be multiples of 8 elements (16-byte rows)");
+  if ((dtype == JL_BF16 && (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16 ||
+                            reinterpret_cast<uintptr_t>(q) % 16)))
+    return fail(JL_ERR_INVALID_ARG, "bf16 q and caches must be 16-byte aligned");
+  const size_t need = jl_bifocal_decode_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim);
+  if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  jl::DecodeCall c{};
+  c.q = q; c.kc = k_cache; c.vc = v_cache;
+  c.sb = stride_b; c.ss = stride_s; c.sh = stride_h;
+  c.o = o; c.lse = lse; c.seq_L = seq_L;
+  c.B = B; c.max_L = max_L; c.Hq = Hq; c.Hkv = Hkv; c.D = head_dim;
+  c.w_pretrained = w_pretrained; c.w0 = w0;
+  c.theta = rope_theta;
+  c.scale = resolve_scale(softmax_scale, head_dim);
+  c.ws = workspace;
+  return hip_status(jl::launch_decode(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_decode launch");
+}
+
+int jl_bifocal_remote_positions(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                int total_q, int w_pretrained, int32_t* pos_out, int32_t* f_out,
+                                int32_t* G_out, void* stream) {
+  if (B < 0 || total_q < 0) return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
+  if (w_pretrained < 1) return fail(JL_ERR_INVALID_ARG, "w_pretrained must be >= 1");
+  if (B == 0) return JL_OK;
+  if (!cu_seqlens_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_q must be non-null");
+  if (!pos_out && !f_out && !G_out) return fail(JL_ERR_INVALID_ARG, "no output given");
+  return hip_status(jl::launch_remote_positions(cu_seqlens_q, cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q,
+                                                B, total_q, w_pretrained, pos_out, f_out, G_out,
+                                                static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_remote_positions launch");
+}
+
+int jl_bifocal_tile_classes(int Lq, int L, int w0, int BM, int BN, uint8_t* cls_out, void* stream) {
+  if (Lq < 0 || L < 0 || Lq > L) return fail(JL_ERR_INVALID_ARG, "need 0 <= Lq <= L");
+  if (w0 < 0) return fail(JL_ERR_INVALID_ARG, "w0 must be >= 0");
+  if (BM < 1 || BN < 1 || BM > 4096 || BN > 4096) return fail(JL_ERR_INVALID_ARG, "BM and BN must lie in [1, 4096]");
+  if (Lq == 0) return JL_OK;
+  if (!cls_out) return fail(JL_ERR_INVALID_ARG, "cls_out must be non-null");
+  return hip_status(jl::launch_tile_classes(Lq, L, w0, BM, BN, cls_out, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_tile_classes launch");
+}
+
+int jl_bifocal_prefill_tile_shape(int dtype, int Hq, int Hkv, int head_dim, int* BM, int* BN) {
+  if (!BM || !BN) return fail(JL_ERR_INVALID_ARG, "BM and BN must be non-null");
+  if (!supported_dtype(dtype)) return fail(JL_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (!supported_dim(head_dim)) return fail(JL_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(JL_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+  if (dtype == JL_BF16) {
+    jl::prefill_bf16_tile_shape(Hq / Hkv, BM, BN);
+  } else {
+    *BM = 64;
+    *BN = 32;
+  }
+  return JL_OK;
+}
+
+const char* jl_status_string(int code) {
+  switch (code) {
+    case JL_OK: return "ok";
+    case JL_ERR_INVALID_ARG: return "invalid argument";
+    case JL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case JL_ERR_WORKSPACE: return "workspace missing or too small";
+    case JL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* jl_last_error(void) { return g_last_error; }
+
+const char* jl_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// Split-K decode of dynamic bifocal RoPE attention on gfx950.
+//
+// "Jet-Long: Efficient Long-Context Extension with Dynamic Bifocal RoPE",
+// section "Inference Efficiency Mechanisms": the KV cache holds the base keys
+// at their exact absolute positions and is never rewritten; the rotation the
+// bifocal scoring needs is applied on the fly to the active query and to each
+// key as it is read, in registers.  Section "Dynamic Bifocal RoPE": a key
+// closer to the query than w0 is scored with classic RoPE, every other key
+// with RoPE at f(x) = floor(x / G), G from the current length L (eq. G, f).
+//
+// Kernel 1 (split): grid (splits, Hkv, B), 4 wavefronts per workgroup.  The
+// workgroup owns a contiguous key range of one sequence and one KV head; each
+// wavefront streams 16-key blocks of it and keeps its own online-softmax state
+// for all query heads of the GQA group, so every cache byte is read once.
+//   bf16: a lane loads 4 x 16 bytes of one key (A operand layout of
+//   v_mfma_f32_16x16x32_f16, rotate-half partners in the same lane), rotates
+//   them at the key's own angle (j if local, f(j) if remote) from the fp32
+//   cos/sin table, and Q K^T for the whole head group is one chain of D/32
+//   MFMAs.  The rotated operands are IEEE half (11 significant bits; bf16
+//   inputs convert exactly), accumulation fp32.  P V runs on the VALU with each lane owning D/64 features of every
+//   head; probabilities are broadcast with v_readlane.
+//   fp32: the same stream with the dot products on the VALU.
+// Kernel 2 (combine): log-sum-exp merge of the per-wavefront partials.
+#include "jl_device.hpp"
+#include "jl_launch.hpp"
+
+namespace jl {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBlk = 16;  // keys per wavefront step
+
+struct Params {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  int64_t sb, ss, sh;
+  float* part;  // [B][Hq][nsplit][kWaves][D + 2]  (O unnormalised, m (log2), l)
+  const int32_t* seq_L;
+  const float2* tab;
+  int B, Hq, Hkv, ratio, nsplit, kps, max_L;
+  int w_pretrained, w0;
+  float scale_log2;
+};
+
+template <int D>
+__device__ __forceinline__ float* part_ptr(const Params& p, int b, int h, int split, int w) {
+  return p.part + ((((static_cast<int64_t>(b) * p.Hq + h) * p.nsplit + split) * kWaves + w) * (D + 2));
+}
+
+// ---------------------------------------------------------------- bf16
+
+template <int D, int NR>
+__global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
+  constexpr int NT = D / 32;    // MFMAs per block (32 features each)
+  constexpr int HT = NT / 2;    // first-half feature groups
+  constexpr int H = D / 2;
+  constexpr int EPL = D / 64;   // V features per lane
+  static_assert(NR <= 16, "one MFMA column per query head");
+
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int L = p.seq_L[b];
+  if (L < 1 || L > p.max_L) return;  // outside the documented contract: left unwritten
+  const int G = group_size(L, p.w_pretrained);
+  const int qpos = L - 1;
+  const int kbeg = split * p.kps;
+  const int kend = min(L, kbeg + p.kps);
+  const int col = lane & 15;  // B column = query head slot; A row = key in block
+  const int g = lane >> 4;    // feature group: features t*32 + g*8 + e
+
+  const uint16_t* kc = static_cast<const uint16_t*>(p.kc) + b * p.sb + hkv * p.sh;
+  const uint16_t* vc = static_cast<const uint16_t*>(p.vc) + b * p.sb + hkv * p.sh;
+
+  // query fragments for all heads of the group, rotated at qpos and f(qpos)
+  f16x8 qlf[NT], qrf[NT];
+  {
+    float x[NT][8];
+    if (col < p.ratio) {
+      const uint16_t* src = static_cast<const uint16_t*>(p.q) +
+                            (static_cast<int64_t>(b) * p.Hq + hkv * p.ratio + col) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + t * 32 + g * 8);
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[t][e] = bf16_bits_to_float(static_cast<uint16_t>(uu[e >> 1] >> (16 * (e & 1))));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
+    }
+    const int fq = qpos / G;
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = t * 32 + g * 8 + e;
+        const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
+        const float2 cr = p.tab[static_cast<int64_t>(fq) * H + kk];
+        const float x1 = x[t][e], x2 = x[t + HT][e];
+        qlf[t][e] = static_cast<_Float16>(x1 * cl.x - x2 * cl.y);
+        qlf[t + HT][e] = static_cast<_Float16>(x2 * cl.x + x1 * cl.y);
+        qrf[t][e] = static_cast<_Float16>(x1 * cr.x - x2 * cr.y);
+        qrf[t + HT][e] = static_cast<_Float16>(x2 * cr.x + x1 * cr.y);
+      }
+  }
+
+  float m_run = -INFINITY;  // lanes with col = head slot carry that head's state
+  float l_run = 0.f;
+  float oacc[NR][EPL];
+#pragma unroll
+  for (int hh = 0; hh < NR; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) oacc[hh][e] = 0.f;
+
+  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += kWaves * kBlk) {
+    // ---- stream K (A layout) and V (lane = features) of 16 keys
+    const int jk = j0 + col;
+    const bool kval = jk < kend;
+    uint4 kr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      kr[t] = kval ? *reinterpret_cast<const uint4*>(kc + jk * p.ss + t * 32 + g * 8) : make_uint4(0, 0, 0, 0);
+    uint32_t vr[kBlk];
+#pragma unroll
+    for (int m = 0; m < kBlk; ++m) {
+      const int jv = j0 + m;
+      if constexpr (EPL == 2)
+        vr[m] = jv < kend ? *reinterpret_cast<const uint32_t*>(vc + jv * p.ss + lane * 2) : 0u;
+      else
+        vr[m] = jv < kend ? static_cast<uint32_t>(vc[jv * p.ss + lane]) : 0u;
+    }
+
+    // ---- rotate each key at its own angle (registers only; cache untouched)
+    const bool klocal = qpos - jk < p.w0;
+    const int kpos = kval ? (klocal ? jk : jk / G) : 0;
+    f16x8 a[NT];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
+      const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = p.tab[static_cast<int64_t>(kpos) * H + t * 32 + g * 8 + e];
+        const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
+        const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
+        a[t][e] = static_cast<_Float16>(x1 * cs.x - x2 * cs.y);
+        a[t + HT][e] = static_cast<_Float16>(x2 * cs.x + x1 * cs.y);
+      }
+    }
+
+    // ---- S = K_rot Q_sel^T: lane (col = head, g) holds keys j0 + g*4 + rr
+    const bool all_remote = qpos - (j0 + kBlk - 1) >= p.w0;
+    const bool all_local = qpos - j0 < p.w0;
+    f32x4 sr = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+    if (!all_local) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qrf[t], sr, 0, 0, 0);
+    }
+    if (!all_remote) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qlf[t], sl, 0, 0, 0);
+    }
+    float s[4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int j = j0 + g * 4 + rr;
+      float v = (qpos - j < p.w0) ? sl[rr] : sr[rr];
+      v = j < kend ? v * p.scale_log2 : -INFINITY;
+      s[rr] = v;
+      bmax = fmaxf(bmax, v);
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(m_run, bmax);
+    const float alpha = exp2f(m_run - m_new);
+    float bsum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      s[rr] = exp2f(s[rr] - m_new);
+      bsum += s[rr];
+    }
+    bsum += __shfl_xor(bsum, 16);
+    bsum += __shfl_xor(bsum, 32);
+    l_run = l_run * alpha + bsum;
+    m_run = m_new;
+
+    // ---- O += P V on the VALU; p(key m, head hh) lives in lane (m/4)*16 + hh, reg m%4
+#pragma unroll
+    for (int hh = 0; hh < NR; ++hh) {
+      const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) oacc[hh][e] *= al;
+    }
+#pragma unroll
+    for (int m = 0; m < kBlk; ++m) {
+      float vf[EPL];
+      vf[0] = __uint_as_float(vr[m] << 16);
+      if constexpr (EPL == 2) vf[1] = __uint_as_float(vr[m] & 0xffff0000u);
+#pragma unroll
+      for (int hh = 0; hh < NR; ++hh) {
+        const float pm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[m & 3]), (m >> 2) * 16 + hh));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) oacc[hh][e] = fmaf(pm, vf[e], oacc[hh][e]);
+      }
+    }
+  }
+
+  // ---- this wavefront's partial state for every head of the group
+#pragma unroll
+  for (int hh = 0; hh < NR; ++hh) {
+    if (hh >= p.ratio) break;
+    float* dst = part_ptr<D>(p, b, hkv * p.ratio + hh, split, w);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[lane * EPL + e] = oacc[hh][e];
+    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), hh));
+    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), hh));
+    if (lane == 0) {
+      dst[D] = mh;
+      dst[D + 1] = lh;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32
+
+template <int D, int NR>
+__global__ __launch_bounds__(kWaves * 64) void split_f32_kernel(Params p) {
+  constexpr int NT = D / 32;
+  constexpr int HT = NT / 2;
+  constexpr int H = D / 2;
+  constexpr int EPL = D / 64;
+  __shared__ float sQ[2][NR][D];  // [0] rotated at qpos, [1] at f(qpos)
+
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int L = p.seq_L[b];
+  if (L < 1 || L > p.max_L) return;  // outside the documented contract: left unwritten
+  const int G = group_size(L, p.w_pretrained);
+  const int qpos = L - 1;
+  const int kbeg = split * p.kps;
+  const int kend = min(L, kbeg + p.kps);
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const float* kc = static_cast<const float*>(p.kc) + b * p.sb + hkv * p.sh;
+  const float* vc = static_cast<const float*>(p.vc) + b * p.sb + hkv * p.sh;
+
+  for (int idx = threadIdx.x; idx < NR * H; idx += kWaves * 64) {
+    const int hh = idx / H;
+    const int kk = idx % H;
+    const bool hv = hh < p.ratio;
+    const float* src = static_cast<const float*>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * p.ratio + (hv ? hh : 0)) * D;
+    const float x1 = hv ? src[kk] : 0.f, x2 = hv ? src[kk + H] : 0.f;
+    const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
+    const float2 cr = p.tab[static_cast<int64_t>(qpos / G) * H + kk];
+    sQ[0][hh][kk] = x1 * cl.x - x2 * cl.y;
+    sQ[0][hh][kk + H] = x2 * cl.x + x1 * cl.y;
+    sQ[1][hh][kk] = x1 * cr.x - x2 * cr.y;
+    sQ[1][hh][kk + H] = x2 * cr.x + x1 * cr.y;
+  }
+  __syncthreads();
+
+  float m_run[NR], l_run[NR], oacc[NR][EPL];
+#pragma unroll
+  for (int hh = 0; hh < NR; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) oacc[hh][e] = 0.f;
+  }
+
+  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += kWaves * kBlk) {
+    const int jk = j0 + col;  // this lane's key
+    const bool kval = jk < kend;
+    const bool klocal = qpos - jk < p.w0;
+    const int kpos = kval ? (klocal ? jk : jk / G) : 0;
+    float kv[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kv[t][e] = kval ? kc[jk * p.ss + t * 32 + g * 8 + e] : 0.f;
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = p.tab[static_cast<int64_t>(kpos) * H + t * 32 + g * 8 + e];
+        const float x1 = kv[t][e], x2 = kv[t + HT][e];
+        kv[t][e] = x1 * cs.x - x2 * cs.y;
+        kv[t + HT][e] = x2 * cs.x + x1 * cs.y;
+      }
+    const float* qsel = klocal ? &sQ[0][0][0] : &sQ[1][0][0];
+    float s[NR];
+#pragma unroll
+    for (int hh = 0; hh < NR; ++hh) {
+      float part = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(kv[t][e], qsel[hh * D + t * 32 + g * 8 + e], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      s[hh] = kval ? part * p.scale_log2 : -INFINITY;
+    }
+#pragma unroll
+    for (int hh = 0; hh < NR; ++hh) {
+      float bm = s[hh];
+      bm = fmaxf(bm, __shfl_xor(bm, 1));
+      bm = fmaxf(bm, __shfl_xor(bm, 2));
+      bm = fmaxf(bm, __shfl_xor(bm, 4));
+      bm = fmaxf(bm, __shfl_xor(bm, 8));
+      const float m_new = fmaxf(m_run[hh], bm);
+      const float alpha = exp2f(m_run[hh] - m_new);
+      s[hh] = exp2f(s[hh] - m_new);
+      float bs = s[hh];
+      bs += __shfl_xor(bs, 1);
+      bs += __shfl_xor(bs, 2);
+      bs += __shfl_xor(bs, 4);
+      bs += __shfl_xor(bs, 8);
+      l_run[hh] = l_run[hh] * alpha + bs;
+      m_run[hh] = m_new;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) oacc[hh][e] *= alpha;
+    }
+#pragma unroll
+    for (int m = 0; m < kBlk; ++m) {
+      const int jv = j0 + m;
+      float vf[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vf[e] = jv < kend ? vc[jv * p.ss + lane * EPL + e] : 0.f;
+#pragma unroll
+      for (int hh = 0; hh < NR; ++hh) {
+        const float pm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[hh]), m));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) oacc[hh][e] = fmaf(pm, vf[e], oacc[hh][e]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int hh = 0; hh < NR; ++hh) {
+    if (hh >= p.ratio) break;
+    float* dst = part_ptr<D>(p, b, hkv * p.ratio + hh, split, w);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[lane * EPL + e] = oacc[hh][e];
+    if (lane == 0) {
+      dst[D] = m_run[hh];
+      dst[D + 1] = l_run[hh];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+
+template <int D>
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int nparts,
+                                                     void* o, float* lse, int bf16) {
+  const int bh = blockIdx.x;  // b * Hq + h
+  const float* pp = part + static_cast<int64_t>(bh) * nparts * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nparts; ++s) M = fmaxf(M, pp[s * (D + 2) + D]);
+  float den = 0.f;
+  for (int s = 0; s < nparts; ++s) {
+    const float ms = pp[s * (D + 2) + D];
+    if (ms != -INFINITY) den += exp2f(ms - M) * pp[s * (D + 2) + D + 1];
+  }
+  const float inv = 1.f / den;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float num = 0.f;
+    for (int s = 0; s < nparts; ++s) {
+      const float ms = pp[s * (D + 2) + D];
+      if (ms != -INFINITY) num += exp2f(ms - M) * pp[s * (D + 2) + d];
+    }
+    const float r = num * inv;
+    if (bf16) static_cast<uint16_t*>(o)[static_cast<int64_t>(bh) * D + d] = float_to_bf16_bits(r);
+    else static_cast<float*>(o)[static_cast<int64_t>(bh) * D + d] = r;
+  }
+  if (lse && threadIdx.x == 0) lse[bh] = (M + log2f(den)) * kLn2;
+}
+
+template <int D, int NR>
+void launch_split(const Params& p, bool bf16, hipStream_t s) {
+  const dim3 grid(p.nsplit, p.Hkv, p.B);
+  if (bf16) hipLaunchKernelGGL((split_bf16_kernel<D, NR>), grid, dim3(kWaves * 64), 0, s, p);
+  else hipLaunchKernelGGL((split_f32_kernel<D, NR>), grid, dim3(kWaves * 64), 0, s, p);
+}
+
+template <int D>
+void launch_split_d(const Params& p, int ratio, bool bf16, hipStream_t s) {
+  if (ratio <= 1) launch_split<D, 1>(p, bf16, s);
+  else if (ratio <= 2) launch_split<D, 2>(p, bf16, s);
+  else if (ratio <= 4) launch_split<D, 4>(p, bf16, s);
+  else if (ratio <= 8) launch_split<D, 8>(p, bf16, s);
+  else launch_split<D, 16>(p, bf16, s);
+}
+
+int keys_per_split(int max_L, int nsplit) {
+  const int per = (max_L + nsplit - 1) / nsplit;
+  return (per + 63) / 64 * 64;
+}
+
+}  // namespace
+
+int decode_num_splits(int B, int max_L, int Hkv) {
+  const int64_t units = static_cast<int64_t>(B) * Hkv;
+  int64_t ns = (2048 + units - 1) / units;
+  const int64_t cap = (static_cast<int64_t>(max_L) + 255) / 256;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  return static_cast<int>(ns);
+}
+
+size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D) {
+  const int ns = decode_num_splits(B, max_L, Hkv);
+  const size_t tab = align_up(static_cast<size_t>(max_L) * (D / 2) * sizeof(float2), 256);
+  const size_t part = static_cast<size_t>(B) * Hq * ns * kWaves * (D + 2) * sizeof(float);
+  return tab + align_up(part, 256);
+}
+
+hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
+  if (c.B == 0) return hipSuccess;
+  const int ns = decode_num_splits(c.B, c.max_L, c.Hkv);
+  char* ws = static_cast<char*>(c.ws);
+  const size_t tab = align_up(static_cast<size_t>(c.max_L) * (c.D / 2) * sizeof(float2), 256);
+  Params p{};
+  p.q = c.q;
+  p.kc = c.kc;
+  p.vc = c.vc;
+  p.sb = c.sb;
+  p.ss = c.ss;
+  p.sh = c.sh;
+  p.part = reinterpret_cast<float*>(ws + tab);
+  p.seq_L = c.seq_L;
+  p.tab = reinterpret_cast<const float2*>(ws);
+  p.B = c.B;
+  p.Hq = c.Hq;
+  p.Hkv = c.Hkv;
+  p.ratio = c.Hq / c.Hkv;
+  p.nsplit = ns;
+  p.kps = keys_per_split(c.max_L, ns);
+  p.max_L = c.max_L;
+  p.w_pretrained = c.w_pretrained;
+  p.w0 = c.w0;
+  p.scale_log2 = c.scale * kLog2e;
+  hipError_t e = launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s);
+  if (e != hipSuccess) return e;
+  const int ratio = c.Hq / c.Hkv;
+  if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);
+  else launch_split_d<64>(p, ratio, bf16, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nparts = ns * kWaves;
+  if (c.D == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace jl

@@ -1,0 +1,62 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jl {
+
+// Arguments of one prefill call after validation (device pointers).
+struct PrefillCall {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B, total_q, total_k, max_q, max_k;
+  int Hq, Hkv, D;
+  int w_pretrained, w0;
+  double theta;
+  float scale;
+  void* ws;
+};
+
+struct DecodeCall {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  int64_t sb, ss, sh;
+  void* o;
+  float* lse;
+  const int32_t* seq_L;
+  int B, max_L, Hq, Hkv, D;
+  int w_pretrained, w0;
+  double theta;
+  float scale;
+  void* ws;
+};
+
+// Workspace layouts (bytes).
+size_t prefill_ws_bytes_bf16(int B, int total_k, int max_k, int Hkv, int D);
+size_t prefill_ws_bytes_f32(int max_k, int D);
+size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D);
+int decode_num_splits(int B, int max_L, int Hkv);
+
+// Query-block height / key-tile width of the bf16 prefill kernel.
+void prefill_bf16_tile_shape(int ratio, int* BM, int* BN);
+
+hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillCall& c, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillCall& c, hipStream_t s);
+hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s);
+hipError_t launch_remote_positions(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q,
+                                   int w_pretrained, int32_t* pos, int32_t* f, int32_t* G,
+                                   hipStream_t s);
+hipError_t launch_tile_classes(int Lq, int L, int w0, int BM, int BN, uint8_t* out, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace jl

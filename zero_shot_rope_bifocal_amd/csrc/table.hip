@@ -1,0 +1,97 @@
+// cos/sin table and integer debug exports.
+//
+// "Jet-Long: Efficient Long-Context Extension with Dynamic Bifocal RoPE",
+// section "Dynamic Bifocal RoPE": eq. G (group size from the current length)
+// and eq. f (remote position = floor(x / G)).
+#include "jl_device.hpp"
+#include "jl_launch.hpp"
+
+namespace jl {
+
+// (cos, sin)(p * theta_k) for p in [0, npos), k in [0, D/2), theta_k =
+// theta^(-2k/D).  Angle and functions in fp64, one rounding to fp32, so the
+// table keeps full fp32 accuracy at positions near 2^17 where an fp32 angle
+// would already be off by ~1e-2 rad.  Layout: float2 tab[p * (D/2) + k].
+__global__ void rope_table_kernel(float2* __restrict__ tab, int npos, int half, double theta,
+                                  double neg2_over_d) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(npos) * half) return;
+  const int p = static_cast<int>(idx / half);
+  const int k = static_cast<int>(idx % half);
+  const double inv = pow(theta, neg2_over_d * k);
+  double s, c;
+  sincos(static_cast<double>(p) * inv, &s, &c);
+  tab[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
+hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s) {
+  const int half = D / 2;
+  const int64_t n = static_cast<int64_t>(npos) * half;
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int blocks = static_cast<int>((n + threads - 1) / threads);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(threads), 0, s, tab, npos, half, theta,
+                     -2.0 / static_cast<double>(D));
+  return hipGetLastError();
+}
+
+// Query positions, remote positions and per-sequence G of a packed batch:
+// sequence b has L_b keys and its Lq_b queries at the last Lq_b positions.
+__global__ void remote_positions_kernel(const int32_t* __restrict__ cu_q,
+                                        const int32_t* __restrict__ cu_k, int B, int total_q,
+                                        int w_pretrained, int32_t* __restrict__ pos,
+                                        int32_t* __restrict__ f, int32_t* __restrict__ Gout) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < B && Gout) Gout[t] = group_size(cu_k[t + 1] - cu_k[t], w_pretrained);
+  if (t >= total_q) return;
+  int lo = 0, hi = B - 1;  // last b with cu_q[b] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int L = cu_k[b + 1] - cu_k[b];
+  const int Lq = cu_q[b + 1] - cu_q[b];
+  const int p = (L - Lq) + (t - cu_q[b]);
+  const int G = group_size(L, w_pretrained);
+  if (pos) pos[t] = p;
+  if (f) f[t] = p / G;
+}
+
+hipError_t launch_remote_positions(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q,
+                                   int w_pretrained, int32_t* pos, int32_t* f, int32_t* G,
+                                   hipStream_t s) {
+  const int n = total_q > B ? total_q : B;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(remote_positions_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cu_q, cu_k,
+                     B, total_q, w_pretrained, pos, f, G);
+  return hipGetLastError();
+}
+
+// The classifier the prefill kernels route on, over one sequence's blocks.
+__global__ void tile_classes_kernel(int Lq, int L, int w0, int BM, int BN, int nqb, int nkb,
+                                    uint8_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(nqb) * nkb) return;
+  const int a = static_cast<int>(idx / nkb);
+  const int bk = static_cast<int>(idx % nkb);
+  const int q_off = L - Lq;
+  const int i0 = q_off + a * BM;
+  const int i1 = min(q_off + Lq, i0 + BM) - 1;
+  const int j0 = bk * BN;
+  const int j1 = min(L, j0 + BN) - 1;
+  out[idx] = static_cast<uint8_t>(classify_tile(i0, i1, j0, j1, w0));
+}
+
+hipError_t launch_tile_classes(int Lq, int L, int w0, int BM, int BN, uint8_t* out,
+                               hipStream_t s) {
+  const int nqb = (Lq + BM - 1) / BM;
+  const int nkb = (L + BN - 1) / BN;
+  const int64_t n = static_cast<int64_t>(nqb) * nkb;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_classes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, Lq, L, w0, BM, BN, nqb, nkb, out);
+  return hipGetLastError();
+}
+
+}  // namespace jl

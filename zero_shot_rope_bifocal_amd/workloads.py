@@ -1,0 +1,145 @@
+"""Named workloads and their seeded synthetic inputs.
+
+This module holds no arithmetic of the attention method: it only draws
+i.i.d. N(0, 1) numbers from seeded numpy PCG64 generators, rounds them to
+bfloat16 (round to nearest even) where the workload is bf16, and packs
+variable-length batches.  The HIP path and the CPU oracle both read the same
+arrays.
+
+The shapes stand in for the setting the Jet-Long pages evaluate (section
+"Experimental Results": Qwen3 models with a 32K native window extended to
+128K); the pages give no head counts, so 32 query / 8 KV heads of dimension
+128 are used.  No benchmark item of any evaluation suite is reproduced.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+WORKLOADS = {
+    # tiny fp32 prefill: parity at 1e-4
+    "tiny_f32": dict(kind="prefill", dtype="f32", lens=[2048], Hq=2, Hkv=2, d=64,
+                     w_pretrained=512, w0=128, theta=1e4, seed=1),
+    # L = w_pretrained: G = 1, must equal classic RoPE causal attention
+    "short_bf16": dict(kind="prefill", dtype="bf16", lens=[32768], Hq=32, Hkv=8, d=128,
+                       w_pretrained=32768, w0=2048, theta=1e6, seed=2),
+    # 128K prefill, G = 4, 64 key rows scaled x4 for peaked attention
+    "long_bf16": dict(kind="prefill", dtype="bf16", lens=[131072], Hq=32, Hkv=8, d=128,
+                      w_pretrained=32768, w0=2048, theta=1e6, seed=3,
+                      peaked_rows=64, peak_seed=1003, peak_scale=4.0),
+    # decode: 16 sequences, full 128K caches, G = 4
+    "decode_bf16": dict(kind="decode", dtype="bf16", B=16, L=131072, Hq=32, Hkv=8, d=128,
+                        w_pretrained=32768, w0=2048, theta=1e6, seed=4),
+    # ragged varlen prefill, G = 1 / 3 / 4
+    "ragged_bf16": dict(kind="prefill", dtype="bf16", lens=[20000, 70000, 131072], Hq=32, Hkv=8,
+                        d=128, w_pretrained=32768, w0=2048, theta=1e6, seed=5),
+}
+
+_CHUNK = 1 << 24
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest even.  The
+    inputs are finite normals, so no NaN handling is needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    fu = u.reshape(-1)
+    fo = out.reshape(-1)
+    for a in range(0, fu.size, _CHUNK):
+        c = fu[a:a + _CHUNK].astype(np.uint64)
+        c += 0x7FFF + ((c >> 16) & 1)
+        fo[a:a + _CHUNK] = (c >> 16).astype(np.uint16)
+    return out
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> their exact float32 values."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normals(rng: np.random.Generator, shape, bf16: bool) -> np.ndarray:
+    n = int(np.prod(shape))
+    if not bf16:
+        return rng.standard_normal(n, dtype=np.float32).reshape(shape)
+    out = np.empty(n, dtype=np.uint16)
+    for a in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - a)
+        out[a:a + m] = bf16_bits(rng.standard_normal(m, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, peak_scale=1.0,
+                   q_lens=None):
+    """Packed batch: q [Tq, Hq, d], k/v [Tk, Hkv, d] in draw order Q, K, V
+    from ``default_rng(seed)``.  bf16 arrays are uint16 bit patterns, f32
+    arrays float32.  ``q_lens`` (default = lens) takes each sequence's queries
+    from its last q_lens[b] positions (the other query rows are never
+    drawn).  ``peaked_rows`` key rows of the first sequence, chosen by
+    ``default_rng(peak_seed)``, are multiplied by ``peak_scale`` in every KV
+    head and feature (a power of two: exact in bf16)."""
+    lens = [int(x) for x in lens]
+    q_lens = lens if q_lens is None else [int(x) for x in q_lens]
+    bf16 = dtype == "bf16"
+    rng = np.random.default_rng(seed)
+    Tq, Tk = sum(q_lens), sum(lens)
+    q = _normals(rng, (Tq, Hq, d), bf16)
+    k = _normals(rng, (Tk, Hkv, d), bf16)
+    v = _normals(rng, (Tk, Hkv, d), bf16)
+    peaks = None
+    if peaked_rows:
+        peaks = np.sort(np.random.default_rng(peak_seed).choice(lens[0], peaked_rows, replace=False))
+        if bf16:
+            vals = bits_to_f32(k[peaks]) * np.float32(peak_scale)
+            k[peaks] = bf16_bits(vals)
+        else:
+            k[peaks] *= np.float32(peak_scale)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k, lens=lens, q_lens=q_lens, peaks=peaks,
+                dtype=dtype, Hq=Hq, Hkv=Hkv, d=d)
+
+
+def decode_inputs(B, S, Hq, Hkv, d, dtype, seed, seq_L=None):
+    """q [B, Hq, d], caches [B, S, Hkv, d] (draw order Q, K, V) and seq_L."""
+    bf16 = dtype == "bf16"
+    rng = np.random.default_rng(seed)
+    q = _normals(rng, (B, Hq, d), bf16)
+    k = _normals(rng, (B, S, Hkv, d), bf16)
+    v = _normals(rng, (B, S, Hkv, d), bf16)
+    if seq_L is None:
+        seq_L = [S] * B
+    return dict(q=q, k=k, v=v, seq_L=np.asarray(seq_L, dtype=np.int32), dtype=dtype,
+                Hq=Hq, Hkv=Hkv, d=d)
+
+
+def workload_inputs(name: str):
+    w = WORKLOADS[name]
+    if w["kind"] == "decode":
+        return decode_inputs(w["B"], w["L"], w["Hq"], w["Hkv"], w["d"], w["dtype"], w["seed"])
+    return prefill_inputs(w["lens"], w["Hq"], w["Hkv"], w["d"], w["dtype"], w["seed"],
+                          w.get("peaked_rows", 0), w.get("peak_seed", 0), w.get("peak_scale", 1.0))
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 values of a generated array (bf16 bits or float32)."""
+    return (bits_to_f32(a) if dtype == "bf16" else a).astype(np.float64)
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda"):
+    """Uploads a generated array as a torch tensor (bfloat16 or float32)."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def sample_rows(L: int, w0: int, w_pretrained: int, seed: int, n_edge: int = 64, n_rand: int = 256):
+    """Stratified query rows of one sequence: first rows, rows around w0,
+    around every multiple of w_pretrained, the last rows and seeded random
+    rows."""
+    rows = set(range(min(L, n_edge)))
+    for c in [w0] + list(range(w_pretrained, L, w_pretrained)):
+        rows.update(range(max(0, c - n_edge // 2), min(L, c + n_edge // 2)))
+    rows.update(range(max(0, L - n_edge), L))
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, L, size=n_rand).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
