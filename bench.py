@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of dynamic bifocal RoPE attention on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input, inputs already
+resident in HBM:
+  * 128K bifocal prefill (bf16 in/out, 32 query / 8 KV heads, d 128,
+    w_pretrained 32768 so G = 4, w0 2048, theta 1e6, 64 key rows x4):
+    jl_bifocal_prefill_prepare (cos/sin table, rotated keys, transposed
+    values) then jl_bifocal_prefill_attend (the attention kernel);
+  * decode of 16 sequences against full 131072-key caches (same heads).
+
+Prints one JSON line.  `value` is the prefill throughput in TFLOP/s over the
+whole prefill call (algorithmic FLOPs = 4 * d * Hq * L(L+1)/2: one logit and
+one PV product per causal pair).  The decode rate (algorithmic bytes = K and
+V read once plus Q and O) is reported beside it.  `roofline` covers the
+dominant kernel (the prefill attention kernel) timed by itself with HIP
+events on the stream it runs on; `cpu_baseline` times the fp64 oracle on a
+bounded sample of query rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_16BIT = 2500.0   # TFLOP/s, MI355X dense fp16 / bf16 MFMA
+PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
+METRIC = "bifocal prefill TFLOP/s @128K (% bf16 MFMA peak); decode HBM GB/s"
+
+
+def prefill_flops(lens, Hq, d):
+    return sum(4.0 * d * Hq * L * (L + 1) / 2 for L in lens)
+
+
+def decode_bytes(B, L, Hq, Hkv, d, elem=2):
+    return B * L * Hkv * d * elem * 2 + 2 * B * Hq * d * elem
+
+
+def source_digest(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, digest: str):
+    """Counter-derived HBM bytes per launch from profiles/, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, budget_s: float):
+    """Times the oracle, as it stands, on query rows of the 128K workload
+    until the time budget is spent.  Returns (TFLOP/s, rows, seconds,
+    threads)."""
+    import numpy as np
+    import oracle
+    from zero_shot_rope_bifocal_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    L = w["lens"][0]
+    k = W.as_f64(inp["k"], "bf16")
+    v = W.as_f64(inp["v"], "bf16")
+    rng = np.random.default_rng(99)
+    order = rng.permutation(L)
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < L:
+        rows = np.sort(order[done:done + 8])
+        q = W.as_f64(inp["q"][rows], "bf16")
+        oracle.bifocal_sequence(q, k, v, rows, L, w["w_pretrained"], w["w0"], w["theta"])
+        flops += sum(4.0 * w["d"] * w["Hq"] * (int(i) + 1) for i in rows)
+        done += len(rows)
+    dt = time.perf_counter() - t0
+    return flops / dt / 1e12, done, dt, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU layout is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import zero_shot_rope_bifocal_amd as jl
+    from zero_shot_rope_bifocal_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wp_ = W.WORKLOADS["long_bf16"]
+    wd = W.WORKLOADS["decode_bf16"]
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log("generating 128K prefill inputs")
+    pin = W.workload_inputs("long_bf16")
+    L = wp_["lens"][0]
+    q = W.to_device(pin["q"], "bf16", dev)
+    k = W.to_device(pin["k"], "bf16", dev)
+    v = W.to_device(pin["v"], "bf16", dev)
+    cu = torch.from_numpy(pin["cu_q"]).to(dev)
+    o = torch.empty_like(q)
+    Hq, Hkv, d = wp_["Hq"], wp_["Hkv"], wp_["d"]
+    ws = torch.empty(jl.prefill_workspace_size(jl.JL_BF16, 1, L, L, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+
+    log("generating decode inputs (16 x 131072 keys)")
+    din = W.workload_inputs("decode_bf16")
+    dq = W.to_device(din["q"], "bf16", dev)
+    dk = W.to_device(din["k"], "bf16", dev)
+    dv = W.to_device(din["v"], "bf16", dev)
+    seq = torch.from_numpy(din["seq_L"]).to(dev)
+    do = torch.empty_like(dq)
+    dws = torch.empty(jl.decode_workspace_size(jl.JL_BF16, wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"]),
+                      dtype=torch.uint8, device=dev)
+    del din["k"], din["v"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        jl.prefill_prepare(k, v, cu, L, wp_["w_pretrained"], wp_["theta"], Hq=Hq, workspace=ws)
+        if ev:
+            ev[1].record()
+        jl.prefill_attend(q, k, v, cu, L, wp_["w_pretrained"], wp_["w0"], wp_["theta"], ws, out=o)
+        if ev:
+            ev[2].record()
+        jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
+        if ev:
+            ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep = [e[0].elapsed_time(e[1]) for e in evs]
+    attn = [e[1].elapsed_time(e[2]) for e in evs]
+    dec = [e[2].elapsed_time(e[3]) for e in evs]
+    tot = [e[0].elapsed_time(e[3]) for e in evs]
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    prep_ms, attn_ms, dec_ms, step_ms = mean(prep), mean(attn), mean(dec), mean(tot)
+    fl = prefill_flops(wp_["lens"], Hq, d)
+    pre_tflops = fl / ((prep_ms + attn_ms) * 1e-3) / 1e12
+    attn_tflops = fl / (attn_ms * 1e-3) / 1e12
+    db = decode_bytes(wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"])
+    dec_gbs = db / (dec_ms * 1e-3) / 1e9
+
+    digest = source_digest("zero_shot_rope_bifocal_amd/csrc/prefill_bf16.hip",
+                           "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
+    traffic = load_traffic("prefill_attn", digest)
+    ddigest = source_digest("zero_shot_rope_bifocal_amd/csrc/decode.hip",
+                            "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
+    dtraffic = load_traffic("decode_split", ddigest)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
+        val, rows, secs, threads = cpu_baseline(pin, wp_, args.cpu_seconds)
+        cpu = {"value": val, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"{rows} random query rows x {Hq} heads of the L=131072 prefill against all "
+                         f"keys, fp64 numpy, {secs:.1f} s"}
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill L=131072 (32/8 heads, d=128, w_pretrained=32768 -> G=4, w0=2048, theta=1e6, "
+                        "64 key rows x4) + decode B=16 x L=131072 (same heads)",
+            "io_dtype": "bf16",
+            "mfma_operands": "f16 (rotated q/k, p, v), fp32 accumulate",
+            "prefill_ms": round(prep_ms + attn_ms, 3),
+            "prefill_prepare_ms": round(prep_ms, 3),
+            "prefill_attend_ms": round(attn_ms, 3),
+            "decode_ms": round(dec_ms, 4),
+            "decode_GBps": round(dec_gbs, 1),
+            "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
+            "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4),
+            "gpu": props.name,
+            "cu_count": props.multi_processor_count,
+            "wall_s_timed": round(wall, 3),
+        },
+        "roofline": {
+            "kernel": "prefill attention (attn_kernel<128,4>)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_MFMA_16BIT,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_MFMA_16BIT, 4),
+            "traffic": traffic,
+        },
+        "roofline_decode": {
+            "kernel": "decode (table + split + combine)",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": PEAK_HBM,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM, 4),
+            "traffic": dtraffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,6 +102,35 @@ int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, flo
                        double rope_theta, float softmax_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two stages jl_bifocal_prefill runs, for callers that attend several
+ * query batches (or several w0 values) to one prepared key set, or that time
+ * the stages apart.
+ *
+ * jl_bifocal_prefill_prepare reads k, v and cu_seqlens_k (meanings as above)
+ * and fills `workspace` with the cos/sin table of positions 0 ..
+ * max_seqlen_k-1 and, for JL_BF16, every key rotated once at its position p
+ * and once at f(p) plus the values in the transposed layout the MFMA kernel
+ * reads (the "Dynamic Bifocal RoPE" rotations, eq. G / eq. f; inputs stay
+ * untouched).  The workspace size is
+ * jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hq, Hkv,
+ * head_dim) for the Hq later used.
+ *
+ * jl_bifocal_prefill_attend runs the attention over a workspace prepared by
+ * a call with the same k, v, dtype, cu_seqlens_k, B, total_k, max_seqlen_k,
+ * Hkv, head_dim, w_pretrained and rope_theta (not checked: a mismatch gives
+ * wrong results, not a fault), with the other arguments as in
+ * jl_bifocal_prefill. */
+int jl_bifocal_prefill_prepare(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
+                               int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
+                               int w_pretrained, double rope_theta, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int jl_bifocal_prefill_attend(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                              double rope_theta, float softmax_scale, const void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace jl_bifocal_decode needs, or 0 on invalid sizes. */
 size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv,
                                         int head_dim);

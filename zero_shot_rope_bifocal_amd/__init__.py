@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "JL_F32", "JL_BF16", "JetLongError", "library_path", "lib",
-    "group_size", "prefill", "decode", "prefill_workspace_size", "decode_workspace_size",
+    "group_size", "prefill", "prefill_prepare", "prefill_attend", "decode", "prefill_workspace_size", "decode_workspace_size",
     "remote_positions", "tile_classes", "prefill_tile_shape", "version",
 ]
 
@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
     L.jl_bifocal_prefill.argtypes = ([c_vp] * 5 + [c_int] + [c_vp] * 2 + [c_int] * 10 +
                                      [c_d, c_f, c_vp, c_sz, c_vp])
     L.jl_bifocal_prefill.restype = c_int
+    L.jl_bifocal_prefill_prepare.argtypes = [c_vp, c_vp, c_int, c_vp] + [c_int] * 6 + [c_d, c_vp, c_sz, c_vp]
+    L.jl_bifocal_prefill_prepare.restype = c_int
+    L.jl_bifocal_prefill_attend.argtypes = L.jl_bifocal_prefill.argtypes
+    L.jl_bifocal_prefill_attend.restype = c_int
     L.jl_bifocal_decode_workspace_size.argtypes = [c_int] * 6
     L.jl_bifocal_decode_workspace_size.restype = c_sz
     L.jl_bifocal_decode.argtypes = ([c_vp] * 3 + [c_i64] * 3 + [c_vp, c_vp, c_int, c_vp] +
@@ -167,6 +171,50 @@ def prefill(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int
         B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, int(w_pretrained), int(w0),
         float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(code)
+    return (out, lse) if return_lse else out
+
+
+def prefill_prepare(k, v, cu_seqlens_k, max_seqlen_k: int, w_pretrained: int, rope_theta: float,
+                    Hq: int | None = None, workspace=None):
+    """First stage of ``prefill``: fills and returns a workspace holding the
+    cos/sin table and (bf16) the rotated keys and transposed values."""
+    torch = _torch()
+    _need_cuda(k, v, cu_seqlens_k)
+    if cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dt = _dtype_code(k)
+    Tk, Hkv, d = k.shape
+    B = cu_seqlens_k.numel() - 1
+    need = prefill_workspace_size(dt, B, Tk, max_seqlen_k, Hq or Hkv, Hkv, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    _check(lib().jl_bifocal_prefill_prepare(_ptr(k), _ptr(v), dt, _ptr(cu_seqlens_k), B, Tk, int(max_seqlen_k),
+                                            Hkv, d, int(w_pretrained), float(rope_theta), _ptr(workspace),
+                                            workspace.numel(), _stream(k.device)))
+    return workspace
+
+
+def prefill_attend(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int,
+                   rope_theta: float, workspace, cu_seqlens_k=None, max_seqlen_k: int | None = None,
+                   softmax_scale: float = 0.0, out=None, lse=None, return_lse: bool = False):
+    """Second stage of ``prefill`` over a workspace from ``prefill_prepare``
+    made with the same keys, values and key-side arguments."""
+    torch = _torch()
+    _need_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, workspace)
+    dt = _dtype_code(q)
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    B = cu_seqlens_q.numel() - 1
+    if max_seqlen_k is None:
+        max_seqlen_k = max_seqlen_q
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    _check(lib().jl_bifocal_prefill_attend(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), dt, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, int(w_pretrained), int(w0),
+        float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

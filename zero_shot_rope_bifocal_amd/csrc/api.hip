@@ -68,12 +68,18 @@ size_t jl_bifocal_prefill_workspace_size(int dtype, int B, int total_k, int max_
   return jl::prefill_ws_bytes_f32(max_seqlen_k, head_dim);
 }
 
-int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
-                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
-                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
-                       int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
-                       float softmax_scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks a full prefill argument list and fills `c`; JL_OK with c.B == 0 or
+// c.total_q == 0 means there is nothing to launch.
+int prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
+                 int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int head_dim,
+                 int w_pretrained, int w0, double rope_theta, float softmax_scale, const void* workspace,
+                 size_t workspace_bytes, jl::PrefillCall* c) {
+  *c = jl::PrefillCall{};
   int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
   if (st != JL_OK) return st;
   if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -89,21 +95,81 @@ int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, flo
   if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  c->q = q; c->k = k; c->v = v; c->o = o; c->lse = lse;
+  c->cu_q = cu_seqlens_q;
+  c->cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
+  c->B = B; c->total_q = total_q; c->total_k = total_k;
+  c->max_q = max_seqlen_q; c->max_k = max_seqlen_k;
+  c->Hq = Hq; c->Hkv = Hkv; c->D = head_dim;
+  c->w_pretrained = w_pretrained; c->w0 = w0;
+  c->theta = rope_theta;
+  c->scale = resolve_scale(softmax_scale, head_dim);
+  c->ws = const_cast<void*>(workspace);
+  return JL_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                       int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
+                       float softmax_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  jl::PrefillCall c;
+  const int st = prefill_args(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                              max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
+                              rope_theta, softmax_scale, workspace, workspace_bytes, &c);
+  if (st != JL_OK || c.B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_prepare(c, s) : jl::launch_prefill_f32_prepare(c, s);
+  if (e != hipSuccess) return hip_status(e, "jl_bifocal_prefill prepare launch");
+  e = dtype == JL_BF16 ? jl::launch_prefill_bf16_attend(c, s) : jl::launch_prefill_f32_attend(c, s);
+  return hip_status(e, "jl_bifocal_prefill attend launch");
+}
+
+int jl_bifocal_prefill_prepare(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
+                               int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
+                               int w_pretrained, double rope_theta, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int st = check_common(dtype, Hkv, Hkv, head_dim, w_pretrained, 0, rope_theta, 0.f);
+  if (st != JL_OK) return st;
+  if (B < 0 || total_k < 0 || max_seqlen_k < 0) return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
+  if (B == 0 || total_k == 0) return JL_OK;
+  if (!k || !v || !cu_seqlens_k) return fail(JL_ERR_INVALID_ARG, "k, v and cu_seqlens_k must be non-null");
+  if (max_seqlen_k < 1) return fail(JL_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 for a non-empty batch");
+  const size_t need = jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hkv, Hkv, head_dim);
+  if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   jl::PrefillCall c{};
-  c.q = q; c.k = k; c.v = v; c.o = o; c.lse = lse;
-  c.cu_q = cu_seqlens_q;
-  c.cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
-  c.B = B; c.total_q = total_q; c.total_k = total_k;
-  c.max_q = max_seqlen_q; c.max_k = max_seqlen_k;
-  c.Hq = Hq; c.Hkv = Hkv; c.D = head_dim;
-  c.w_pretrained = w_pretrained; c.w0 = w0;
+  c.k = k; c.v = v; c.cu_k = cu_seqlens_k;
+  c.B = B; c.total_k = total_k; c.max_k = max_seqlen_k;
+  c.Hq = Hkv; c.Hkv = Hkv; c.D = head_dim;
+  c.w_pretrained = w_pretrained;
   c.theta = rope_theta;
-  c.scale = resolve_scale(softmax_scale, head_dim);
   c.ws = workspace;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16(c, s) : jl::launch_prefill_f32(c, s);
-  return hip_status(e, "jl_bifocal_prefill launch");
+  const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_prepare(c, s) : jl::launch_prefill_f32_prepare(c, s);
+  return hip_status(e, "jl_bifocal_prefill_prepare launch");
+}
+
+int jl_bifocal_prefill_attend(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                              double rope_theta, float softmax_scale, const void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  jl::PrefillCall c;
+  const int st = prefill_args(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                              max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
+                              rope_theta, softmax_scale, workspace, workspace_bytes, &c);
+  if (st != JL_OK || c.B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_attend(c, s) : jl::launch_prefill_f32_attend(c, s);
+  return hip_status(e, "jl_bifocal_prefill_attend launch");
 }
 
 size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv, int head_dim) {

@@ -49,8 +49,12 @@ int decode_num_splits(int B, int max_L, int Hkv);
 void prefill_bf16_tile_shape(int ratio, int* BM, int* BN);
 
 hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s);
-hipError_t launch_prefill_bf16(const PrefillCall& c, hipStream_t s);
-hipError_t launch_prefill_f32(const PrefillCall& c, hipStream_t s);
+// Prefill in two stages on one workspace: prepare (cos/sin table; for bf16
+// also the rotated key copies and transposed values) and attend.
+hipError_t launch_prefill_bf16_prepare(const PrefillCall& c, hipStream_t s);
+hipError_t launch_prefill_bf16_attend(const PrefillCall& c, hipStream_t s);
+hipError_t launch_prefill_f32_prepare(const PrefillCall& c, hipStream_t s);
+hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s);
 hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s);
 hipError_t launch_remote_positions(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q,
                                    int w_pretrained, int32_t* pos, int32_t* f, int32_t* G,

@@ -11,9 +11,9 @@
 // Two kernels per call, both on the caller's stream:
 //  1. prep: every key row is rotated once at its true position p and once at
 //     f(p) (head-major rows padded per sequence to a multiple of 64) and V is
-//     laid out transposed per head, [d][key], so that the PV product can read
-//     8 keys of one feature as two 8-byte LDS reads.  The raw K/V inputs are
-//     only read.
+//     laid out transposed per head, [d][key], with each 16-key group in the
+//     k-slot order of the PV MFMA, so that one A fragment (8 keys of one
+//     feature) is one 16-byte LDS read.  The raw K/V inputs are only read.
 //  Operand precision: the MFMA operands (rotated Q and K, P, V) are IEEE
 //  half, accumulation is fp32.  bf16 inputs convert to half exactly (within
 //  +-65504), and rotation keeps each pair's norm, while a rotated value
@@ -85,7 +85,11 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
   const int pos = static_cast<int>(pos64);
   uint16_t* kl_row = p.kl + (static_cast<int64_t>(hk) * p.tpad + r) * D;
   uint16_t* kr_row = p.kr + (static_cast<int64_t>(hk) * p.tpad + r) * D;
-  uint16_t* vt_col = p.vt + static_cast<int64_t>(hk) * D * p.tpad + r;
+  // V^T column of this key: inside each 16-key group the quads are stored in
+  // the order 0, 2, 1, 3, which is the order the PV MFMA's k slots take them
+  const int64_t rq = (r >> 2) & 3;
+  const int64_t vcol = (r & ~15LL) | (((rq == 1) ? 2 : (rq == 2) ? 1 : rq) << 2) | (r & 3);
+  uint16_t* vt_col = p.vt + static_cast<int64_t>(hk) * D * p.tpad + vcol;
   if (pos < L) {
     const int64_t tok = p.cu_k[b] + pos;
     const int G = group_size(L, p.w_pretrained);
@@ -142,23 +146,254 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 
 // ---------------------------------------------------------------- attention
 
+constexpr int kVSTR = kBN + 8;  // LDS row stride of V^T tiles (elements, 16-byte rows)
+
+// Per-thread registers of one prefetched tile (global -> registers -> LDS).
+// Named members, not arrays: an indexed private array here is promoted to
+// LDS by the compiler before unrolling, which doubles the LDS traffic.
+struct TileRegs {
+  uint4 kr0, kr1, kl0, kl1, v0, v1;
+};
+
+// chunk c of a key tile: row c / (D/8), 16-byte column c % (D/8)
+template <int D>
+__device__ __forceinline__ uint4 ld_k(const uint16_t* base, int64_t row0, int c) {
+  return *reinterpret_cast<const uint4*>(base + (row0 + c / (D / 8)) * D + (c % (D / 8)) * 8);
+}
+// chunk c of a V^T tile: feature row c / 8, 16-byte column c % 8
+__device__ __forceinline__ uint4 ld_v(const uint16_t* base, int64_t tpad, int64_t row0, int c) {
+  return *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(c / (kBN / 8)) * tpad + row0 + (c % (kBN / 8)) * 8);
+}
+
+// D = 128: 1024 chunks per K tile and per V^T tile -> 2 per thread each;
+// D = 64: 512 -> 1 per thread.
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* kr_base, const uint16_t* kl_base,
+                                          const uint16_t* vt_base, int64_t tpad, int64_t row0, int cls,
+                                          int tid) {
+  const int base = cls & 3;
+  if (base != kLocal) {
+    t.kr0 = ld_k<D>(kr_base, row0, tid);
+    if constexpr (D == 128) t.kr1 = ld_k<D>(kr_base, row0, tid + kThreads);
+  }
+  if (base != kRemote) {
+    t.kl0 = ld_k<D>(kl_base, row0, tid);
+    if constexpr (D == 128) t.kl1 = ld_k<D>(kl_base, row0, tid + kThreads);
+  }
+  t.v0 = ld_v(vt_base, tpad, row0, tid);
+  if constexpr (D == 128) t.v1 = ld_v(vt_base, tpad, row0, tid + kThreads);
+}
+
+template <int D>
+__device__ __forceinline__ void st_k(uint16_t* s, int c, uint4 val) {
+  *reinterpret_cast<uint4*>(s + (c / (D / 8)) * (D + 8) + (c % (D / 8)) * 8) = val;
+}
+__device__ __forceinline__ void st_v(uint16_t* s, int c, uint4 val) {
+  *reinterpret_cast<uint4*>(s + (c / (kBN / 8)) * kVSTR + (c % (kBN / 8)) * 8) = val;
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* sKr, uint16_t* sKl, uint16_t* sV,
+                                           int cls, int tid) {
+  const int base = cls & 3;
+  if (base != kLocal) {
+    st_k<D>(sKr, tid, t.kr0);
+    if constexpr (D == 128) st_k<D>(sKr, tid + kThreads, t.kr1);
+  }
+  if (base != kRemote) {
+    st_k<D>(sKl, tid, t.kl0);
+    if constexpr (D == 128) st_k<D>(sKl, tid + kThreads, t.kl1);
+  }
+  st_v(sV, tid, t.v0);
+  if constexpr (D == 128) st_v(sV, tid + kThreads, t.v1);
+}
+
+// Raw bf16 query fragment of this lane (features ks*16 + g*8 + e), or zeros.
+template <int D>
+__device__ __forceinline__ void load_query(float (&x)[D / 16][8], const uint16_t* src, bool valid, int g) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (valid) u = *reinterpret_cast<const uint4*>(src + ks * 16 + g * 8);
+    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[ks][e] = bf16_bits_to_float(static_cast<uint16_t>(uu[e >> 1] >> (16 * (e & 1))));
+  }
+}
+
+// Rotates this lane's query fragment (features ks*16 + g*8 + e) at position
+// `pos` and scales it by c = softmax_scale * log2(e), so that the MFMA
+// accumulators come out as log2-domain logits.
+template <int D>
+__device__ __forceinline__ void rotate_query(f16x8 (&out)[D / 16], const float (&x)[D / 16][8],
+                                             const float2* __restrict__ tab, int pos, int g, float c) {
+  constexpr int KS = D / 16;
+  const float2* row = tab + static_cast<int64_t>(pos) * (D / 2);
+#pragma unroll
+  for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 cs = row[ks * 16 + g * 8 + e];
+      const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
+      out[ks][e] = static_cast<_Float16>((x1 * cs.x - x2 * cs.y) * c);
+      out[ks + KS / 2][e] = static_cast<_Float16>((x2 * cs.x + x1 * cs.y) * c);
+    }
+}
+
+// Value of lane l ^ 32 combined with lane l's own (max or sum), on the VALU.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// P^T (half) from log2-domain scores already relative to the row's running
+// max; returns the row sum of the rounded probabilities (they are what P V
+// multiplies).
+__device__ __forceinline__ float probs(const float (&t)[2][16], f16x8 (&pf)[4]) {
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pf[ks2][e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(t[ks2 >> 1][(ks2 & 1) * 8 + e]));
+  const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  float rs = 0.f;
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const f16x2 pr = {pf[ks2][e], pf[ks2][e + 1]};
+      rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+    }
+  return xhalf_sum(rs);
+}
+
+// O^T += V^T P^T: one 16-byte LDS read per A fragment (each 16-key group of a
+// V^T row is stored in the MFMA k-slot order by the prep pass).
+template <int D>
+__device__ __forceinline__ void pv(const uint16_t* __restrict__ v_lane, const f16x8 (&pf)[4],
+                                   f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2)
+      acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *reinterpret_cast<const f16x8*>(v_lane + mb * 32 * kVSTR + ks2 * 16), pf[ks2], acc[mb], 0, 0, 0);
+}
+
+// S^T for a 64-key tile: two 32-key blocks, accumulators start at `init`.
+template <int D>
+__device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f16x8 (&qf)[D / 16],
+                                   f32x16 init, f32x16 (&sc)[2]) {
+  constexpr int KSTR = D + 8;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(k_lane + kb * 32 * KSTR),
+                                                   qf[0], init, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < D / 16; ++ks)
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *reinterpret_cast<const f16x8*>(k_lane + kb * 32 * KSTR + ks * 16), qf[ks], sc[kb], 0, 0, 0);
+  }
+}
+
+// Fast path of an all-remote, unmasked tile.  The score accumulators start at
+// -m_run, so they come out relative to the running max.  If any row's max
+// rose by more than 8 (log2) the tile is left to the slow path and nothing is
+// changed; otherwise the stale max stands (probabilities stay below 2^8, far
+// inside half range) and no rescale of O is needed.
+template <int D>
+__device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
+                                          const uint16_t* __restrict__ v_lane,
+                                          const f16x8 (&qrf)[D / 16], f32x16 (&acc)[D / 32], float m_run,
+                                          float& l_run) {
+  f32x16 init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) init[r] = -m_run;
+  f32x16 sc[2];
+  qk<D>(kr_lane, qrf, init, sc);
+  float mx = sc[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+  mx = xhalf_max(mx);
+  if (__any(mx > 8.f)) return false;
+  float t[2][16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[kb][r] = sc[kb][r];
+  f16x8 pf[4];
+  l_run += probs(t, pf);
+  pv<D>(v_lane, pf, acc);
+  return true;
+}
+
+// General tile (any class, optional mask) with an exact running-max update.
+// USE_R / USE_L select which logit sets the tile needs (remote / local / both
+// when it straddles the window edge); MASK adds the causal and
+// end-of-sequence mask.  Lane (r32, g) holds query qi; accumulator register r
+// of key block kb holds key j0g + kb*32 + (r/4)*8 + r%4 (j0g = tile start +
+// g*4).
+template <int D, bool USE_R, bool USE_L, bool MASK>
+__device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
+                                          const uint16_t* __restrict__ kl_lane,
+                                          const uint16_t* __restrict__ v_lane,
+                                          const f16x8 (&qrf)[D / 16], const f16x8 (&qlf)[D / 16],
+                                          f32x16 (&acc)[D / 32], float& m_run, float& l_run,
+                                          int qi, int j0g, int L, int w0) {
+  const f32x16 zero = {};
+  f32x16 sr[2], sl[2];
+  if constexpr (USE_R) qk<D>(kr_lane, qrf, zero, sr);
+  if constexpr (USE_L) qk<D>(kl_lane, qlf, zero, sl);
+  float t[2][16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = j0g + kb * 32 + (r >> 2) * 8 + (r & 3);
+      float s;
+      if constexpr (USE_R && USE_L) s = (qi - kj < w0) ? sl[kb][r] : sr[kb][r];
+      else if constexpr (USE_R) s = sr[kb][r];
+      else s = sl[kb][r];
+      if constexpr (MASK) s = (kj > qi || kj >= L) ? -INFINITY : s;
+      t[kb][r] = s;
+      mx = fmaxf(mx, s);
+    }
+  mx = xhalf_max(mx);
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  l_run *= alpha;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+  m_run = m_new;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[kb][r] -= m_new;
+  f16x8 pf[4];
+  l_run += probs(t, pf);
+  pv<D>(v_lane, pf, acc);
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   constexpr int RB = kWaves / HPW;  // 32-row blocks per query head
   constexpr int ROWS = 32 * RB;     // query positions per workgroup
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int MB = D / 32;        // 32-feature blocks of O^T
-  constexpr int H = D / 2;
   constexpr int KSTR = D + 8;       // LDS row stride of key tiles (elements)
-  constexpr int VSTR = kBN + 4;     // LDS row stride of V^T tiles (elements)
-  constexpr int KCH = kBN * D / 8;  // 16-byte chunks per key tile
-  constexpr int KPT = (KCH + kThreads - 1) / kThreads;
-  constexpr int VCH = D * kBN / 8;
-  constexpr int VPT = (VCH + kThreads - 1) / kThreads;
 
   __shared__ __attribute__((aligned(16))) uint16_t sKr[2][kBN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sKl[2][kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kVSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,219 +429,111 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int g = lane >> 5;
   const int qi = i0 + rb * 32 + r32;
   const bool qvalid = qi <= i1;
+  const int pl = qvalid ? qi : 0;
 
-  // ---- query fragments rotated at p (local) and f(p) (remote)
-  f16x8 qlf[KS], qrf[KS];
+  // ---- query fragment rotated at f(p); the local one is built after the
+  // all-remote tiles so that it does not occupy registers during them
+  const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid ? qi - q_off : 0)) * p.Hq + h) * D;
+  f16x8 qrf[KS], qlf[KS];
   {
     float x[KS][8];
-    if (qvalid) {
-      const uint16_t* src = p.q + (static_cast<int64_t>(qbeg + qi - q_off) * p.Hq + h) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 u = *reinterpret_cast<const uint4*>(src + ks * 16 + g * 8);
-        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x[ks][e] = bf16_bits_to_float(static_cast<uint16_t>(uu[e >> 1] >> (16 * (e & 1))));
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[ks][e] = 0.f;
-    }
-    const int pl = qvalid ? qi : 0;
-    const int pr = pl / G;
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = ks * 16 + g * 8 + e;
-        const float2 cl = p.tab[static_cast<int64_t>(pl) * H + kk];
-        const float2 cr = p.tab[static_cast<int64_t>(pr) * H + kk];
-        const float x1 = x[ks][e];
-        const float x2 = x[ks + KS / 2][e];
-        qlf[ks][e] = static_cast<_Float16>(x1 * cl.x - x2 * cl.y);
-        qlf[ks + KS / 2][e] = static_cast<_Float16>(x2 * cl.x + x1 * cl.y);
-        qrf[ks][e] = static_cast<_Float16>(x1 * cr.x - x2 * cr.y);
-        qrf[ks + KS / 2][e] = static_cast<_Float16>(x2 * cr.x + x1 * cr.y);
-      }
-    }
+    load_query<D>(x, qsrc, qvalid, g);
+    rotate_query<D>(qrf, x, p.tab, pl / G, g, p.scale_log2);
   }
 
-  // ---- tile loader (global -> registers -> LDS), double buffered
   const uint16_t* kr_base = p.kr + static_cast<int64_t>(hkv) * p.tpad * D;
   const uint16_t* kl_base = p.kl + static_cast<int64_t>(hkv) * p.tpad * D;
   const uint16_t* vt_base = p.vt + static_cast<int64_t>(hkv) * D * p.tpad;
-  uint4 rk[KPT], rkl[KPT], rv[VPT];
+  const int kr_off = r32 * KSTR + g * 8;
+  const int v_off = r32 * kVSTR + g * 8;
 
-  auto tile_class = [&](int kt) {
-    const int j0 = kt * kBN;
-    return classify_tile(i0, i1, j0, min(L, j0 + kBN) - 1, p.w0);
-  };
-  auto issue = [&](int kt, int cls) {
-    const int64_t row0 = krow0 + static_cast<int64_t>(kt) * kBN;
-    const int base = cls & 3;
-    if (base != kLocal) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < KCH)
-          rk[i] = *reinterpret_cast<const uint4*>(kr_base + (row0 + c / (D / 8)) * D + (c % (D / 8)) * 8);
-      }
-    }
-    if (base != kRemote) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < KCH)
-          rkl[i] = *reinterpret_cast<const uint4*>(kl_base + (row0 + c / (D / 8)) * D + (c % (D / 8)) * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < VCH)
-        rv[i] = *reinterpret_cast<const uint4*>(vt_base + static_cast<int64_t>(c / (kBN / 8)) * p.tpad + row0 + (c % (kBN / 8)) * 8);
-    }
-  };
-  auto commit = [&](int buf, int cls) {
-    const int base = cls & 3;
-    if (base != kLocal) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < KCH) *reinterpret_cast<uint4*>(&sKr[buf][(c / (D / 8)) * KSTR + (c % (D / 8)) * 8]) = rk[i];
-      }
-    }
-    if (base != kRemote) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < KCH) *reinterpret_cast<uint4*>(&sKl[buf][(c / (D / 8)) * KSTR + (c % (D / 8)) * 8]) = rkl[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < VCH) {
-        uint16_t* dst = &sV[buf][(c / (kBN / 8)) * VSTR + (c % (kBN / 8)) * 8];
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
-      }
-    }
-  };
-
-  // ---- main loop
-  float m_run = -INFINITY;  // running max, log2 domain
+  float m_run = -INFINITY;  // running max (log2 domain, possibly stale by < 8)
   float l_run = 0.f;
   f32x16 acc[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
 
   const int nkt = i1 / kBN + 1;
-  int cls = tile_class(0);
-  issue(0, cls);
-  commit(0, cls);
+  // tiles [0, nrem) are all-remote; classes never return to remote later
+  int nrem = 0;
+  while (nrem < nkt && (classify_tile(i0, i1, nrem * kBN, min(L, nrem * kBN + kBN) - 1, p.w0) & 3) == kRemote) ++nrem;
+  auto cls_of = [&](int kt) { return classify_tile(i0, i1, kt * kBN, min(L, kt * kBN + kBN) - 1, p.w0); };
+
+  TileRegs tr;
+  int cls = cls_of(0);
+  load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
+  store_tile<D>(tr, sKr[0], sKl[0], sV[0], cls, tid);
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    int ncls = 0;
-    if (kt + 1 < nkt) {
-      ncls = tile_class(kt + 1);
-      issue(kt + 1, ncls);
-    }
-    const int base = cls & 3;
-    const int j0 = kt * kBN;
-    const bool need_mask = (cls & kDiag) || (j0 + kBN > L);
-
-    f32x16 sr[2], sl[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sr[kb][r] = 0.f; sl[kb][r] = 0.f; }
-    if (base != kLocal) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(&sKr[buf][(kb * 32 + r32) * KSTR + ks * 16 + g * 8]);
-          sr[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qrf[ks], sr[kb], 0, 0, 0);
-        }
-    }
-    if (base != kRemote) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(&sKl[buf][(kb * 32 + r32) * KSTR + ks * 16 + g * 8]);
-          sl[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qlf[ks], sl[kb], 0, 0, 0);
-        }
-    }
-
-    // routing, masking, scaling (lane = one query; register r = one key)
-    float t[2][16];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kj = j0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        float s;
-        if (base == kRemote) s = sr[kb][r];
-        else if (base == kLocal) s = sl[kb][r];
-        else s = (qi - kj < p.w0) ? sl[kb][r] : sr[kb][r];
-        s *= p.scale_log2;
-        if (need_mask && (kj > qi || kj >= L)) s = -INFINITY;
-        t[kb][r] = s;
-        mx = fmaxf(mx, s);
+  // ---- all-remote tiles: remote query only.  The inner loop is the fast
+  // path; a tile it declines (first tile, a large max increase, a masked
+  // tile) is redone by the slow path, which then re-enters the fast loop.
+  int kt = 0;
+  while (kt < nrem) {
+    for (; kt < nrem; ++kt) {
+      const int buf = kt & 1;
+      if ((cls & kDiag) || kt * kBN + kBN > L) break;
+      if (!tile_fast<D>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run)) break;
+      int ncls = 0;
+      if (kt + 1 < nkt) {
+        ncls = cls_of(kt + 1);
+        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        t[kb][r] = exp2f(t[kb][r] - m_new);
-        rs += t[kb][r];
+      __syncthreads();
+      cls = ncls;
+    }
+    if (kt < nrem) {
+      const int buf = kt & 1;
+      const int j0g = kt * kBN + g * 4;
+      if ((cls & kDiag) || kt * kBN + kBN > L)
+        tile_slow<D, true, false, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
+                                        m_run, l_run, qi, j0g, L, p.w0);
+      else
+        tile_slow<D, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
+                                         m_run, l_run, qi, j0g, L, p.w0);
+      int ncls = 0;
+      if (kt + 1 < nkt) {
+        ncls = cls_of(kt + 1);
+        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       }
-    rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      __syncthreads();
+      cls = ncls;
+      ++kt;
+    }
+  }
 
-    // P^T fragments: k-step ks2 covers tile keys ks2*16 .. ks2*16+15
-    f16x8 pf[4];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[ks2][e] = static_cast<_Float16>(t[ks2 >> 1][(ks2 & 1) * 8 + e]);
-
-    // O^T += V^T P^T; A slot s of lane half g holds key ks2*16 + (s/4)*8 + g*4 + s%4,
-    // the same key the P^T slot s holds
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) {
-        const uint16_t* vr = &sV[buf][(mb * 32 + r32) * VSTR + ks2 * 16 + g * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const f16x8 a = __builtin_bit_cast(f16x8, u);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks2], acc[mb], 0, 0, 0);
+  // ---- window-edge and local tiles: the local query joins (slow path)
+  if (nrem < nkt) {
+    {
+      float x[KS][8];
+      load_query<D>(x, qsrc, qvalid, g);
+      rotate_query<D>(qlf, x, p.tab, pl, g, p.scale_log2);
+    }
+    for (kt = nrem; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      const int j0g = kt * kBN + g * 4;
+      const bool mask = (cls & kDiag) || kt * kBN + kBN > L;
+      const uint16_t* krl = sKr[buf] + kr_off;
+      const uint16_t* kll = sKl[buf] + kr_off;
+      const uint16_t* vl = sV[buf] + v_off;
+      if ((cls & 3) == kLocal) {
+        if (mask) tile_slow<D, false, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else tile_slow<D, false, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+      } else {
+        if (mask) tile_slow<D, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else tile_slow<D, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       }
-
-    if (kt + 1 < nkt) commit(buf ^ 1, ncls);
-    __syncthreads();
-    cls = ncls;
+      int ncls = 0;
+      if (kt + 1 < nkt) {
+        ncls = cls_of(kt + 1);
+        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+      }
+      __syncthreads();
+      cls = ncls;
+    }
   }
 
   // ---- epilogue: lane holds query qi, features mb*32 + (r/4)*8 + g*4 + r%4
@@ -455,8 +582,7 @@ size_t prefill_ws_bytes_bf16(int B, int total_k, int max_k, int Hkv, int D) {
   return tab + 3 * align_up(rows, 256);
 }
 
-hipError_t launch_prefill_bf16(const PrefillCall& c, hipStream_t s) {
-  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+static Params make_params(const PrefillCall& c) {
   const int64_t tpad = prefill_tpad(c.B, c.total_k);
   char* ws = static_cast<char*>(c.ws);
   const size_t tab_bytes = align_up(static_cast<size_t>(c.max_k) * (c.D / 2) * sizeof(float2), 256);
@@ -488,16 +614,24 @@ hipError_t launch_prefill_bf16(const PrefillCall& c, hipStream_t s) {
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
+  return p;
+}
 
-  hipError_t e = launch_rope_table(reinterpret_cast<float2*>(ws), c.max_k, c.D, c.theta, s);
+hipError_t launch_prefill_bf16_prepare(const PrefillCall& c, hipStream_t s) {
+  if (c.B == 0 || c.total_k == 0) return hipSuccess;
+  const Params p = make_params(c);
+  hipError_t e = launch_rope_table(static_cast<float2*>(c.ws), c.max_k, c.D, c.theta, s);
   if (e != hipSuccess) return e;
-  if (c.total_k > 0) {
-    const dim3 pg(static_cast<unsigned>((tpad + 63) / 64), c.Hkv, c.D / 16);
-    if (c.D == 128) hipLaunchKernelGGL(prep_kernel<128>, pg, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL(prep_kernel<64>, pg, dim3(64), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const dim3 pg(static_cast<unsigned>((p.tpad + 63) / 64), c.Hkv, c.D / 16);
+  if (c.D == 128) hipLaunchKernelGGL(prep_kernel<128>, pg, dim3(64), 0, s, p);
+  else hipLaunchKernelGGL(prep_kernel<64>, pg, dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16_attend(const PrefillCall& c, hipStream_t s) {
+  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+  const Params p = make_params(c);
+  const int hpw = heads_per_wg(p.ratio);
   if (c.D == 128) {
     if (hpw == 4) return launch_attn<128, 4>(p, p.nqb, s);
     if (hpw == 2) return launch_attn<128, 2>(p, p.nqb, s);

@@ -168,7 +168,12 @@ size_t prefill_ws_bytes_f32(int max_k, int D) {
   return align_up(static_cast<size_t>(max_k) * (D / 2) * sizeof(float2), 256);
 }
 
-hipError_t launch_prefill_f32(const PrefillCall& c, hipStream_t s) {
+hipError_t launch_prefill_f32_prepare(const PrefillCall& c, hipStream_t s) {
+  if (c.B == 0 || c.total_k == 0) return hipSuccess;
+  return launch_rope_table(static_cast<float2*>(c.ws), c.max_k, c.D, c.theta, s);
+}
+
+hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s) {
   if (c.total_q == 0 || c.B == 0) return hipSuccess;
   Params p{};
   p.q = static_cast<const float*>(c.q);
@@ -190,8 +195,6 @@ hipError_t launch_prefill_f32(const PrefillCall& c, hipStream_t s) {
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
-  hipError_t e = launch_rope_table(static_cast<float2*>(c.ws), c.max_k, c.D, c.theta, s);
-  if (e != hipSuccess) return e;
   const dim3 grid(p.nqb, c.Hq, c.B);
   if (c.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, p);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, p);

@@ -13,6 +13,9 @@ The shapes stand in for the setting the Jet-Long pages evaluate (section
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 WORKLOADS = {
@@ -34,20 +37,24 @@ WORKLOADS = {
                         d=128, w_pretrained=32768, w0=2048, theta=1e6, seed=5),
 }
 
-_CHUNK = 1 << 24
+_CHUNK = 1 << 22
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _bf16_from_f32(x: np.ndarray) -> np.ndarray:
+    u = x.view(np.uint32)
+    return ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bfloat16 bit patterns (uint16), round to nearest even.  The
-    inputs are finite normals, so no NaN handling is needed."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    out = np.empty(u.shape, dtype=np.uint16)
-    fu = u.reshape(-1)
-    fo = out.reshape(-1)
-    for a in range(0, fu.size, _CHUNK):
-        c = fu[a:a + _CHUNK].astype(np.uint64)
-        c += 0x7FFF + ((c >> 16) & 1)
-        fo[a:a + _CHUNK] = (c >> 16).astype(np.uint16)
+    inputs are finite, so the 32-bit sum cannot overflow and no NaN handling
+    is needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    fx, fo = x.reshape(-1), out.reshape(-1)
+    for a in range(0, fx.size, _CHUNK):
+        fo[a:a + _CHUNK] = _bf16_from_f32(fx[a:a + _CHUNK])
     return out
 
 
@@ -56,21 +63,35 @@ def bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-def _normals(rng: np.random.Generator, shape, bf16: bool) -> np.ndarray:
+def _normals(seed: int, stream: int, shape, bf16: bool) -> np.ndarray:
+    """N(0, 1) draws for one array of a workload.  Element chunk c (2^22
+    elements, row-major order) comes from PCG64 seeded with
+    SeedSequence(seed, spawn_key=(stream, c)), so the values do not depend on
+    how many threads fill the array."""
     n = int(np.prod(shape))
-    if not bf16:
-        return rng.standard_normal(n, dtype=np.float32).reshape(shape)
-    out = np.empty(n, dtype=np.uint16)
-    for a in range(0, n, _CHUNK):
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+
+    def fill(c):
+        a = c * _CHUNK
         m = min(_CHUNK, n - a)
-        out[a:a + m] = bf16_bits(rng.standard_normal(m, dtype=np.float32))
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, c))))
+        x = rng.standard_normal(m, dtype=np.float32)
+        out[a:a + m] = _bf16_from_f32(x) if bf16 else x
+
+    nchunks = -(-n // _CHUNK)
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with cf.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
 def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, peak_scale=1.0,
                    q_lens=None):
-    """Packed batch: q [Tq, Hq, d], k/v [Tk, Hkv, d] in draw order Q, K, V
-    from ``default_rng(seed)``.  bf16 arrays are uint16 bit patterns, f32
+    """Packed batch: q [Tq, Hq, d], k/v [Tk, Hkv, d] drawn as streams 0, 1, 2
+    of ``seed`` (see ``_normals``).  bf16 arrays are uint16 bit patterns, f32
     arrays float32.  ``q_lens`` (default = lens) takes each sequence's queries
     from its last q_lens[b] positions (the other query rows are never
     drawn).  ``peaked_rows`` key rows of the first sequence, chosen by
@@ -79,11 +100,10 @@ def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, pe
     lens = [int(x) for x in lens]
     q_lens = lens if q_lens is None else [int(x) for x in q_lens]
     bf16 = dtype == "bf16"
-    rng = np.random.default_rng(seed)
     Tq, Tk = sum(q_lens), sum(lens)
-    q = _normals(rng, (Tq, Hq, d), bf16)
-    k = _normals(rng, (Tk, Hkv, d), bf16)
-    v = _normals(rng, (Tk, Hkv, d), bf16)
+    q = _normals(seed, 0, (Tq, Hq, d), bf16)
+    k = _normals(seed, 1, (Tk, Hkv, d), bf16)
+    v = _normals(seed, 2, (Tk, Hkv, d), bf16)
     peaks = None
     if peaked_rows:
         peaks = np.sort(np.random.default_rng(peak_seed).choice(lens[0], peaked_rows, replace=False))
@@ -99,12 +119,11 @@ def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, pe
 
 
 def decode_inputs(B, S, Hq, Hkv, d, dtype, seed, seq_L=None):
-    """q [B, Hq, d], caches [B, S, Hkv, d] (draw order Q, K, V) and seq_L."""
+    """q [B, Hq, d], caches [B, S, Hkv, d] (streams 0, 1, 2 of ``seed``) and seq_L."""
     bf16 = dtype == "bf16"
-    rng = np.random.default_rng(seed)
-    q = _normals(rng, (B, Hq, d), bf16)
-    k = _normals(rng, (B, S, Hkv, d), bf16)
-    v = _normals(rng, (B, S, Hkv, d), bf16)
+    q = _normals(seed, 0, (B, Hq, d), bf16)
+    k = _normals(seed, 1, (B, S, Hkv, d), bf16)
+    v = _normals(seed, 2, (B, S, Hkv, d), bf16)
     if seq_L is None:
         seq_L = [S] * B
     return dict(q=q, k=k, v=v, seq_L=np.asarray(seq_L, dtype=np.int32), dtype=dtype,
