@@ -99,6 +99,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one stage only (for profiling); the JSON line then covers that stage")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -118,38 +122,53 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    log("generating 128K prefill inputs")
-    pin = W.workload_inputs("long_bf16")
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
     L = wp_["lens"][0]
-    q = W.to_device(pin["q"], "bf16", dev)
-    k = W.to_device(pin["k"], "bf16", dev)
-    v = W.to_device(pin["v"], "bf16", dev)
-    cu = torch.from_numpy(pin["cu_q"]).to(dev)
-    o = torch.empty_like(q)
     Hq, Hkv, d = wp_["Hq"], wp_["Hkv"], wp_["d"]
-    ws = torch.empty(jl.prefill_workspace_size(jl.JL_BF16, 1, L, L, Hq, Hkv, d), dtype=torch.uint8, device=dev)
-
-    log("generating decode inputs (16 x 131072 keys)")
-    din = W.workload_inputs("decode_bf16")
-    dq = W.to_device(din["q"], "bf16", dev)
-    dk = W.to_device(din["k"], "bf16", dev)
-    dv = W.to_device(din["v"], "bf16", dev)
-    seq = torch.from_numpy(din["seq_L"]).to(dev)
-    do = torch.empty_like(dq)
-    dws = torch.empty(jl.decode_workspace_size(jl.JL_BF16, wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"]),
-                      dtype=torch.uint8, device=dev)
-    del din["k"], din["v"]
+    pin = None
+    if do_prefill:
+        log("generating 128K prefill inputs")
+        pin = W.workload_inputs("long_bf16")
+        q = W.to_device(pin["q"], "bf16", dev)
+        k = W.to_device(pin["k"], "bf16", dev)
+        v = W.to_device(pin["v"], "bf16", dev)
+        cu = torch.from_numpy(pin["cu_q"]).to(dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(jl.prefill_workspace_size(jl.JL_BF16, 1, L, L, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    if do_decode:
+        log("generating decode inputs (16 x 131072 keys)")
+        din = W.workload_inputs("decode_bf16")
+        dq = W.to_device(din["q"], "bf16", dev)
+        dk = W.to_device(din["k"], "bf16", dev)
+        dv = W.to_device(din["v"], "bf16", dev)
+        seq = torch.from_numpy(din["seq_L"]).to(dev)
+        do = torch.empty_like(dq)
+        dws = torch.empty(jl.decode_workspace_size(jl.JL_BF16, wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"]),
+                          dtype=torch.uint8, device=dev)
+        del din
+    if args.copy_mib:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
+        # calibrate the counters against bytes actually moved
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        jl.prefill_prepare(k, v, cu, L, wp_["w_pretrained"], wp_["theta"], Hq=Hq, workspace=ws)
+        if do_prefill:
+            jl.prefill_prepare(k, v, cu, L, wp_["w_pretrained"], wp_["theta"], Hq=Hq, workspace=ws)
         if ev:
             ev[1].record()
-        jl.prefill_attend(q, k, v, cu, L, wp_["w_pretrained"], wp_["w0"], wp_["theta"], ws, out=o)
+        if do_prefill:
+            jl.prefill_attend(q, k, v, cu, L, wp_["w_pretrained"], wp_["w0"], wp_["theta"], ws, out=o)
         if ev:
             ev[2].record()
-        jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
+        if do_decode:
+            jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
         if ev:
             ev[3].record()
 
@@ -172,10 +191,10 @@ def main():
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     prep_ms, attn_ms, dec_ms, step_ms = mean(prep), mean(attn), mean(dec), mean(tot)
     fl = prefill_flops(wp_["lens"], Hq, d)
-    pre_tflops = fl / ((prep_ms + attn_ms) * 1e-3) / 1e12
-    attn_tflops = fl / (attn_ms * 1e-3) / 1e12
+    pre_tflops = fl / ((prep_ms + attn_ms) * 1e-3) / 1e12 if do_prefill else 0.0
+    attn_tflops = fl / (attn_ms * 1e-3) / 1e12 if do_prefill else 0.0
     db = decode_bytes(wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"])
-    dec_gbs = db / (dec_ms * 1e-3) / 1e9
+    dec_gbs = db / (dec_ms * 1e-3) / 1e9 if do_decode else 0.0
 
     digest = source_digest("zero_shot_rope_bifocal_amd/csrc/prefill_bf16.hip",
                            "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
@@ -185,7 +204,7 @@ def main():
     dtraffic = load_traffic("decode_split", ddigest)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and do_prefill:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
         val, rows, secs, threads = cpu_baseline(pin, wp_, args.cpu_seconds)
         cpu = {"value": val, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -218,6 +237,7 @@ def main():
             "decode_GBps": round(dec_gbs, 1),
             "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
             "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4),
+            "stages": args.only or "prefill+decode",
             "gpu": props.name,
             "cu_count": props.multi_processor_count,
             "wall_s_timed": round(wall, 3),

@@ -28,7 +28,8 @@ namespace jl {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // bf16 split kernel: one workgroup = 8 wavefronts
+constexpr int kWavesF32 = 4;
 constexpr int kBlk = 16;  // keys per wavefront step
 
 struct Params {
@@ -36,17 +37,19 @@ struct Params {
   const void* kc;
   const void* vc;
   int64_t sb, ss, sh;
-  float* part;  // [B][Hq][nsplit][kWaves][D + 2]  (O unnormalised, m (log2), l)
+  float* part;  // [B][Hq][nsplit][slots][D + 2]  (O unnormalised, m (log2), l)
   const int32_t* seq_L;
   const float2* tab;
   int B, Hq, Hkv, ratio, nsplit, kps, max_L;
+  int wph;    // wavefronts per KV head in a workgroup (bf16 split kernel)
+  int slots;  // partial states per (sequence, head, split)
   int w_pretrained, w0;
   float scale_log2;
 };
 
 template <int D>
 __device__ __forceinline__ float* part_ptr(const Params& p, int b, int h, int split, int w) {
-  return p.part + ((((static_cast<int64_t>(b) * p.Hq + h) * p.nsplit + split) * kWaves + w) * (D + 2));
+  return p.part + ((((static_cast<int64_t>(b) * p.Hq + h) * p.nsplit + split) * p.slots + w) * (D + 2));
 }
 
 // ---------------------------------------------------------------- bf16
@@ -59,11 +62,17 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
   constexpr int EPL = D / 64;   // V features per lane
   static_assert(NR <= 16, "one MFMA column per query head");
 
-  const int split = blockIdx.x;
-  const int hkv = blockIdx.y;
-  const int b = blockIdx.z;
+  // one workgroup = one key range of one sequence for `hw` KV heads, `wph`
+  // wavefronts per head: with 8 KV heads every wave streams its own 256-byte
+  // slice of the same 2 KB cache rows, and all waves read the same cos/sin rows
+  const int hw = kWaves / p.wph;
+  const int hgrp = blockIdx.x % (p.Hkv / hw);
+  const int b = blockIdx.x / (p.Hkv / hw);
+  const int split = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int wid = threadIdx.x >> 6;
+  const int hkv = hgrp * hw + wid / p.wph;
+  const int w = wid % p.wph;  // this wave's slot among the waves of its head
   const int L = p.seq_L[b];
   if (L < 1 || L > p.max_L) return;  // outside the documented contract: left unwritten
   const int G = group_size(L, p.w_pretrained);
@@ -76,7 +85,8 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
   const uint16_t* kc = static_cast<const uint16_t*>(p.kc) + b * p.sb + hkv * p.sh;
   const uint16_t* vc = static_cast<const uint16_t*>(p.vc) + b * p.sb + hkv * p.sh;
 
-  // query fragments for all heads of the group, rotated at qpos and f(qpos)
+  // query fragments for all heads of the group, rotated at qpos and f(qpos),
+  // with the softmax scale (log2 domain) folded in
   f16x8 qlf[NT], qrf[NT];
   {
     float x[NT][8];
@@ -97,6 +107,7 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
         for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
     }
     const int fq = qpos / G;
+    const float c = p.scale_log2;
 #pragma unroll
     for (int t = 0; t < HT; ++t)
 #pragma unroll
@@ -105,10 +116,10 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
         const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
         const float2 cr = p.tab[static_cast<int64_t>(fq) * H + kk];
         const float x1 = x[t][e], x2 = x[t + HT][e];
-        qlf[t][e] = static_cast<_Float16>(x1 * cl.x - x2 * cl.y);
-        qlf[t + HT][e] = static_cast<_Float16>(x2 * cl.x + x1 * cl.y);
-        qrf[t][e] = static_cast<_Float16>(x1 * cr.x - x2 * cr.y);
-        qrf[t + HT][e] = static_cast<_Float16>(x2 * cr.x + x1 * cr.y);
+        qlf[t][e] = static_cast<_Float16>((x1 * cl.x - x2 * cl.y) * c);
+        qlf[t + HT][e] = static_cast<_Float16>((x2 * cl.x + x1 * cl.y) * c);
+        qrf[t][e] = static_cast<_Float16>((x1 * cr.x - x2 * cr.y) * c);
+        qrf[t + HT][e] = static_cast<_Float16>((x2 * cr.x + x1 * cr.y) * c);
       }
   }
 
@@ -120,25 +131,30 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) oacc[hh][e] = 0.f;
 
-  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += kWaves * kBlk) {
-    // ---- stream K (A layout) and V (lane = features) of 16 keys
-    const int jk = j0 + col;
-    const bool kval = jk < kend;
+  const int step = p.wph * kBlk;
+  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += step) {
+    // ---- stream K (A layout: lane = key j0 + col, features t*32 + g*8 ..)
+    // and V (lane = features lane*EPL .. of each of the 16 keys)
     uint4 kr[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      kr[t] = kval ? *reinterpret_cast<const uint4*>(kc + jk * p.ss + t * 32 + g * 8) : make_uint4(0, 0, 0, 0);
     uint32_t vr[kBlk];
+    {
+      const int jk = j0 + col;
 #pragma unroll
-    for (int m = 0; m < kBlk; ++m) {
-      const int jv = j0 + m;
-      if constexpr (EPL == 2)
-        vr[m] = jv < kend ? *reinterpret_cast<const uint32_t*>(vc + jv * p.ss + lane * 2) : 0u;
-      else
-        vr[m] = jv < kend ? static_cast<uint32_t>(vc[jv * p.ss + lane]) : 0u;
+      for (int t = 0; t < NT; ++t)
+        kr[t] = jk < kend ? *reinterpret_cast<const uint4*>(kc + jk * p.ss + t * 32 + g * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < kBlk; ++m) {
+        const int jv = j0 + m;
+        if constexpr (EPL == 2)
+          vr[m] = jv < kend ? *reinterpret_cast<const uint32_t*>(vc + jv * p.ss + lane * 2) : 0u;
+        else
+          vr[m] = jv < kend ? static_cast<uint32_t>(vc[jv * p.ss + lane]) : 0u;
+      }
     }
 
     // ---- rotate each key at its own angle (registers only; cache untouched)
+    const int jk = j0 + col;
+    const bool kval = jk < kend;
     const bool klocal = qpos - jk < p.w0;
     const int kpos = kval ? (klocal ? jk : jk / G) : 0;
     f16x8 a[NT];
@@ -146,13 +162,20 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
     for (int t = 0; t < HT; ++t) {
       const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
       const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
+      const float4* cs4 = reinterpret_cast<const float4*>(p.tab + static_cast<int64_t>(kpos) * H + t * 32 + g * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = p.tab[static_cast<int64_t>(kpos) * H + t * 32 + g * 8 + e];
-        const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
-        const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
-        a[t][e] = static_cast<_Float16>(x1 * cs.x - x2 * cs.y);
-        a[t + HT][e] = static_cast<_Float16>(x2 * cs.x + x1 * cs.y);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float4 cs = cs4[e2];  // (cos, sin) of features 2*e2 and 2*e2 + 1
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int e = e2 * 2 + hh;
+          const float cc = hh ? cs.z : cs.x;
+          const float ss = hh ? cs.w : cs.y;
+          const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
+          const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
+          a[t][e] = static_cast<_Float16>(x1 * cc - x2 * ss);
+          a[t + HT][e] = static_cast<_Float16>(x2 * cc + x1 * ss);
+        }
       }
     }
 
@@ -174,18 +197,18 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
     for (int rr = 0; rr < 4; ++rr) {
       const int j = j0 + g * 4 + rr;
       float v = (qpos - j < p.w0) ? sl[rr] : sr[rr];
-      v = j < kend ? v * p.scale_log2 : -INFINITY;
+      v = j < kend ? v : -INFINITY;
       s[rr] = v;
       bmax = fmaxf(bmax, v);
     }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float m_new = fmaxf(m_run, bmax);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float bsum = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      s[rr] = exp2f(s[rr] - m_new);
+      s[rr] = __builtin_amdgcn_exp2f(s[rr] - m_new);
       bsum += s[rr];
     }
     bsum += __shfl_xor(bsum, 16);
@@ -233,16 +256,16 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
 // ---------------------------------------------------------------- fp32
 
 template <int D, int NR>
-__global__ __launch_bounds__(kWaves * 64) void split_f32_kernel(Params p) {
+__global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
   constexpr int NT = D / 32;
   constexpr int HT = NT / 2;
   constexpr int H = D / 2;
   constexpr int EPL = D / 64;
   __shared__ float sQ[2][NR][D];  // [0] rotated at qpos, [1] at f(qpos)
 
-  const int split = blockIdx.x;
-  const int hkv = blockIdx.y;
-  const int b = blockIdx.z;
+  const int hkv = blockIdx.x % p.Hkv;
+  const int b = blockIdx.x / p.Hkv;
+  const int split = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int L = p.seq_L[b];
@@ -256,7 +279,7 @@ __global__ __launch_bounds__(kWaves * 64) void split_f32_kernel(Params p) {
   const float* kc = static_cast<const float*>(p.kc) + b * p.sb + hkv * p.sh;
   const float* vc = static_cast<const float*>(p.vc) + b * p.sb + hkv * p.sh;
 
-  for (int idx = threadIdx.x; idx < NR * H; idx += kWaves * 64) {
+  for (int idx = threadIdx.x; idx < NR * H; idx += kWavesF32 * 64) {
     const int hh = idx / H;
     const int kk = idx % H;
     const bool hv = hh < p.ratio;
@@ -280,7 +303,7 @@ __global__ __launch_bounds__(kWaves * 64) void split_f32_kernel(Params p) {
     for (int e = 0; e < EPL; ++e) oacc[hh][e] = 0.f;
   }
 
-  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += kWaves * kBlk) {
+  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += kWavesF32 * kBlk) {
     const int jk = j0 + col;  // this lane's key
     const bool kval = jk < kend;
     const bool klocal = qpos - jk < p.w0;
@@ -362,37 +385,64 @@ __global__ __launch_bounds__(kWaves * 64) void split_f32_kernel(Params p) {
 
 // ---------------------------------------------------------------- combine
 
+// Log-sum-exp merge of the partial states of one (sequence, query head):
+// weights 2^(m_s - M) are formed once, then each thread sums one feature
+// over the partials (coalesced reads).
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int nparts,
-                                                     void* o, float* lse, int bf16) {
+__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nparts, void* o,
+                                                    float* lse, int bf16) {
+  constexpr int kMaxParts = 1024;
+  __shared__ float sw[kMaxParts];
+  __shared__ float sred[D / 64];
+  __shared__ float sM, sden;
   const int bh = blockIdx.x;  // b * Hq + h
+  const int t = threadIdx.x;
   const float* pp = part + static_cast<int64_t>(bh) * nparts * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nparts; ++s) M = fmaxf(M, pp[s * (D + 2) + D]);
+  float mx = -INFINITY;
+  for (int s = t; s < nparts; s += D) mx = fmaxf(mx, pp[s * (D + 2) + D]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) sred[t >> 6] = mx;
+  __syncthreads();
+  if (t == 0) {
+    float M = sred[0];
+    for (int i = 1; i < D / 64; ++i) M = fmaxf(M, sred[i]);
+    sM = M;
+  }
+  __syncthreads();
+  const float M = sM;
   float den = 0.f;
-  for (int s = 0; s < nparts; ++s) {
+  for (int s = t; s < nparts; s += D) {
     const float ms = pp[s * (D + 2) + D];
-    if (ms != -INFINITY) den += exp2f(ms - M) * pp[s * (D + 2) + D + 1];
+    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    sw[s] = wgt;
+    den += wgt * pp[s * (D + 2) + D + 1];
   }
-  const float inv = 1.f / den;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float num = 0.f;
-    for (int s = 0; s < nparts; ++s) {
-      const float ms = pp[s * (D + 2) + D];
-      if (ms != -INFINITY) num += exp2f(ms - M) * pp[s * (D + 2) + d];
-    }
-    const float r = num * inv;
-    if (bf16) static_cast<uint16_t*>(o)[static_cast<int64_t>(bh) * D + d] = float_to_bf16_bits(r);
-    else static_cast<float*>(o)[static_cast<int64_t>(bh) * D + d] = r;
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  __syncthreads();
+  if ((t & 63) == 0) sred[t >> 6] = den;
+  __syncthreads();
+  if (t == 0) {
+    float dd = 0.f;
+    for (int i = 0; i < D / 64; ++i) dd += sred[i];
+    sden = dd;
   }
-  if (lse && threadIdx.x == 0) lse[bh] = (M + log2f(den)) * kLn2;
+  __syncthreads();
+  float num = 0.f;
+  for (int s = 0; s < nparts; ++s) num = fmaf(sw[s], pp[s * (D + 2) + t], num);
+  const float r = num / sden;
+  if (bf16) static_cast<uint16_t*>(o)[static_cast<int64_t>(bh) * D + t] = float_to_bf16_bits(r);
+  else static_cast<float*>(o)[static_cast<int64_t>(bh) * D + t] = r;
+  if (lse && t == 0) lse[bh] = (M + log2f(sden)) * kLn2;
 }
 
 template <int D, int NR>
 void launch_split(const Params& p, bool bf16, hipStream_t s) {
-  const dim3 grid(p.nsplit, p.Hkv, p.B);
-  if (bf16) hipLaunchKernelGGL((split_bf16_kernel<D, NR>), grid, dim3(kWaves * 64), 0, s, p);
-  else hipLaunchKernelGGL((split_f32_kernel<D, NR>), grid, dim3(kWaves * 64), 0, s, p);
+  if (bf16) {
+    const int hw = kWaves / p.wph;
+    hipLaunchKernelGGL((split_bf16_kernel<D, NR>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((split_f32_kernel<D, NR>), dim3(p.B * p.Hkv, p.nsplit), dim3(kWavesF32 * 64), 0, s, p);
+  }
 }
 
 template <int D>
@@ -411,11 +461,18 @@ int keys_per_split(int max_L, int nsplit) {
 
 }  // namespace
 
+// Key-range splits per (sequence, KV head): about 8192 streaming wavefronts
+// in all (two per SIMD slot at the split kernel's occupancy), each split at
+// least 256 keys, and at most 128 splits (the combine merges up to 1024
+// partial states).
 int decode_num_splits(int B, int max_L, int Hkv) {
-  const int64_t units = static_cast<int64_t>(B) * Hkv;
-  int64_t ns = (2048 + units - 1) / units;
+  int hw = 1;
+  while (hw < kWaves && Hkv % (hw * 2) == 0) hw *= 2;
+  const int64_t waves = static_cast<int64_t>(B) * Hkv * (kWaves / hw);
+  int64_t ns = (8192 + waves - 1) / waves;
   const int64_t cap = (static_cast<int64_t>(max_L) + 255) / 256;
   if (ns > cap) ns = cap;
+  if (ns > 128) ns = 128;
   if (ns < 1) ns = 1;
   return static_cast<int>(ns);
 }
@@ -423,7 +480,7 @@ int decode_num_splits(int B, int max_L, int Hkv) {
 size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D) {
   const int ns = decode_num_splits(B, max_L, Hkv);
   const size_t tab = align_up(static_cast<size_t>(max_L) * (D / 2) * sizeof(float2), 256);
-  const size_t part = static_cast<size_t>(B) * Hq * ns * kWaves * (D + 2) * sizeof(float);
+  const size_t part = static_cast<size_t>(B) * Hq * ns * kWaves * (D + 2) * sizeof(float);  // slots <= kWaves
   return tab + align_up(part, 256);
 }
 
@@ -449,19 +506,28 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.nsplit = ns;
   p.kps = keys_per_split(c.max_L, ns);
   p.max_L = c.max_L;
+  {
+    int hw = 1;  // KV heads per bf16 workgroup: largest power of two dividing Hkv, at most 8
+    while (hw < kWaves && c.Hkv % (hw * 2) == 0) hw *= 2;
+    p.wph = kWaves / hw;
+  }
+  p.slots = bf16 ? p.wph : kWavesF32;
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
-  hipError_t e = launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s);
+  // rows a decode reads: remote positions (all below w_pretrained) and each
+  // sequence's local window
+  hipError_t e = launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B, c.w0,
+                                        c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s);
   if (e != hipSuccess) return e;
   const int ratio = c.Hq / c.Hkv;
   if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);
   else launch_split_d<64>(p, ratio, bf16, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nparts = ns * kWaves;
+  const int nparts = ns * p.slots;
   if (c.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(128), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
   else
     hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
   return hipGetLastError();

@@ -34,8 +34,10 @@ namespace jl {
 namespace {
 
 constexpr int kBN = 64;     // keys per tile
-constexpr int kWaves = 8;   // wavefronts per workgroup
-constexpr int kThreads = kWaves * 64;
+constexpr int kWaves = 8;   // 32-row blocks per workgroup
+#ifndef JL_PREFILL_NRB
+#define JL_PREFILL_NRB 1
+#endif
 
 struct Params {
   const uint16_t* q;
@@ -145,15 +147,21 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- attention
+//
+// A workgroup covers one KV head, HPW of its query heads and 256 / HPW query
+// positions; NW = 8 / NRB wavefronts each own one head and NRB blocks of 32
+// positions.  With NRB = 2 every K / V fragment read from LDS feeds two MFMAs
+// (one per row block), which halves LDS traffic per FLOP; the wave then runs
+// alone on its SIMD with up to 512 registers.
 
 constexpr int kVSTR = kBN + 8;  // LDS row stride of V^T tiles (elements, 16-byte rows)
 
-// Per-thread registers of one prefetched tile (global -> registers -> LDS).
-// Named members, not arrays: an indexed private array here is promoted to
-// LDS by the compiler before unrolling, which doubles the LDS traffic.
-struct TileRegs {
-  uint4 kr0, kr1, kl0, kl1, v0, v1;
-};
+#ifndef JL_PIN_SCHEDULE
+#define JL_PIN_SCHEDULE 0
+#endif
+// Pin an LDS read-ahead order on the MFMA loops (measured: no gain at one
+// row block per wave, so off by default).
+constexpr bool kPinSchedule = JL_PIN_SCHEDULE != 0;
 
 // chunk c of a key tile: row c / (D/8), 16-byte column c % (D/8)
 template <int D>
@@ -164,26 +172,6 @@ __device__ __forceinline__ uint4 ld_k(const uint16_t* base, int64_t row0, int c)
 __device__ __forceinline__ uint4 ld_v(const uint16_t* base, int64_t tpad, int64_t row0, int c) {
   return *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(c / (kBN / 8)) * tpad + row0 + (c % (kBN / 8)) * 8);
 }
-
-// D = 128: 1024 chunks per K tile and per V^T tile -> 2 per thread each;
-// D = 64: 512 -> 1 per thread.
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* kr_base, const uint16_t* kl_base,
-                                          const uint16_t* vt_base, int64_t tpad, int64_t row0, int cls,
-                                          int tid) {
-  const int base = cls & 3;
-  if (base != kLocal) {
-    t.kr0 = ld_k<D>(kr_base, row0, tid);
-    if constexpr (D == 128) t.kr1 = ld_k<D>(kr_base, row0, tid + kThreads);
-  }
-  if (base != kRemote) {
-    t.kl0 = ld_k<D>(kl_base, row0, tid);
-    if constexpr (D == 128) t.kl1 = ld_k<D>(kl_base, row0, tid + kThreads);
-  }
-  t.v0 = ld_v(vt_base, tpad, row0, tid);
-  if constexpr (D == 128) t.v1 = ld_v(vt_base, tpad, row0, tid + kThreads);
-}
-
 template <int D>
 __device__ __forceinline__ void st_k(uint16_t* s, int c, uint4 val) {
   *reinterpret_cast<uint4*>(s + (c / (D / 8)) * (D + 8) + (c % (D / 8)) * 8) = val;
@@ -192,20 +180,46 @@ __device__ __forceinline__ void st_v(uint16_t* s, int c, uint4 val) {
   *reinterpret_cast<uint4*>(s + (c / (kBN / 8)) * kVSTR + (c % (kBN / 8)) * 8) = val;
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* sKr, uint16_t* sKl, uint16_t* sV,
-                                           int cls, int tid) {
+// Per-thread registers of one prefetched tile (global -> registers -> LDS):
+// CPT 16-byte chunks of each of K (remote), K (local) and V^T.
+template <int CPT>
+struct TileRegs {
+  uint4 kr[CPT], kl[CPT], v[CPT];
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void load_tile(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
+                                          const uint16_t* kl_base, const uint16_t* vt_base, int64_t tpad,
+                                          int64_t row0, int cls, int tid) {
+  constexpr int CPT = D * kBN / 8 / NT;
   const int base = cls & 3;
   if (base != kLocal) {
-    st_k<D>(sKr, tid, t.kr0);
-    if constexpr (D == 128) st_k<D>(sKr, tid + kThreads, t.kr1);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) t.kr[i] = ld_k<D>(kr_base, row0, tid + i * NT);
   }
   if (base != kRemote) {
-    st_k<D>(sKl, tid, t.kl0);
-    if constexpr (D == 128) st_k<D>(sKl, tid + kThreads, t.kl1);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) t.kl[i] = ld_k<D>(kl_base, row0, tid + i * NT);
   }
-  st_v(sV, tid, t.v0);
-  if constexpr (D == 128) st_v(sV, tid + kThreads, t.v1);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) t.v[i] = ld_v(vt_base, tpad, row0, tid + i * NT);
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void store_tile(const TileRegs<D * kBN / 8 / NT>& t, uint16_t* sKr, uint16_t* sKl,
+                                           uint16_t* sV, int cls, int tid) {
+  constexpr int CPT = D * kBN / 8 / NT;
+  const int base = cls & 3;
+  if (base != kLocal) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) st_k<D>(sKr, tid + i * NT, t.kr[i]);
+  }
+  if (base != kRemote) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) st_k<D>(sKl, tid + i * NT, t.kl[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) st_v(sV, tid + i * NT, t.v[i]);
 }
 
 // Raw bf16 query fragment of this lane (features ks*16 + g*8 + e), or zeros.
@@ -221,9 +235,9 @@ __device__ __forceinline__ void load_query(float (&x)[D / 16][8], const uint16_t
   }
 }
 
-// Rotates this lane's query fragment (features ks*16 + g*8 + e) at position
-// `pos` and scales it by c = softmax_scale * log2(e), so that the MFMA
-// accumulators come out as log2-domain logits.
+// Rotates this lane's query fragment at position `pos` and scales it by
+// c = softmax_scale * log2(e), so that the MFMA accumulators come out as
+// log2-domain logits.
 template <int D>
 __device__ __forceinline__ void rotate_query(f16x8 (&out)[D / 16], const float (&x)[D / 16][8],
                                              const float2* __restrict__ tab, int pos, int g, float c) {
@@ -271,32 +285,70 @@ __device__ __forceinline__ float probs(const float (&t)[2][16], f16x8 (&pf)[4]) 
   return xhalf_sum(rs);
 }
 
-// O^T += V^T P^T: one 16-byte LDS read per A fragment (each 16-key group of a
-// V^T row is stored in the MFMA k-slot order by the prep pass).
-template <int D>
-__device__ __forceinline__ void pv(const uint16_t* __restrict__ v_lane, const f16x8 (&pf)[4],
-                                   f32x16 (&acc)[D / 32]) {
+// O^T += V^T P^T for NRB row blocks: every V^T fragment (one 16-byte LDS read:
+// each 16-key group of a V^T row is stored in the MFMA k-slot order by the
+// prep pass) feeds NRB MFMAs.  Same read-ahead schedule as qk().
+template <int D, int NRB>
+__device__ __forceinline__ void pv(const uint16_t* __restrict__ v_lane, const f16x8 (&pf)[NRB][4],
+                                   f32x16 (&acc)[NRB][D / 32]) {
+  constexpr int MB = D / 32;
+  constexpr int NF = 4 * MB;  // fragments: (k-step, feature block), feature block fastest
+  constexpr int PF = 4;
+  f16x8 a[NF];
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
+  for (int f = 0; f < NF; ++f)
+    a[f] = *reinterpret_cast<const f16x8*>(v_lane + (f % MB) * 32 * kVSTR + (f / MB) * 16);
 #pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2)
-      acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          *reinterpret_cast<const f16x8*>(v_lane + mb * 32 * kVSTR + ks2 * 16), pf[ks2], acc[mb], 0, 0, 0);
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      acc[rb][f % MB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], pf[rb][f / MB], acc[rb][f % MB], 0, 0, 0);
+  if constexpr (kPinSchedule) {
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int f = 0; f < NF - PF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
+  }
 }
 
-// S^T for a 64-key tile: two 32-key blocks, accumulators start at `init`.
-template <int D>
-__device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f16x8 (&qf)[D / 16],
-                                   f32x16 init, f32x16 (&sc)[2]) {
+// S^T of a 64-key tile for NRB row blocks (two 32-key blocks each); the
+// accumulators start at `init`.  Every K fragment feeds NRB MFMAs.  The
+// schedule keeps LDS reads PF fragments ahead of the MFMAs that consume them,
+// so the read latency hides behind MFMA work instead of stalling each MFMA.
+template <int D, int NRB>
+__device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f16x8 (&qf)[NRB][D / 16],
+                                   const float (&init)[NRB], f32x16 (&sc)[NRB][2]) {
   constexpr int KSTR = D + 8;
+  constexpr int KS = D / 16;
+  constexpr int NF = 2 * KS;  // fragments per tile: (key block, k-step)
+  constexpr int PF = 4;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(k_lane + kb * 32 * KSTR),
-                                                   qf[0], init, 0, 0, 0);
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int ks = 1; ks < D / 16; ++ks)
-      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          *reinterpret_cast<const f16x8*>(k_lane + kb * 32 * KSTR + ks * 16), qf[ks], sc[kb], 0, 0, 0);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[rb][kb][r] = init[rb];
+  f16x8 a[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    a[f] = *reinterpret_cast<const f16x8*>(k_lane + (f & 1) * 32 * KSTR + (f >> 1) * 16);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      sc[rb][f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], qf[rb][f >> 1], sc[rb][f & 1], 0, 0, 0);
+  // schedule: PF reads, then (NRB MFMAs, one read) until the reads run out
+  if constexpr (kPinSchedule) {
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int f = 0; f < NF - PF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
   }
 }
 
@@ -305,91 +357,106 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
 // rose by more than 8 (log2) the tile is left to the slow path and nothing is
 // changed; otherwise the stale max stands (probabilities stay below 2^8, far
 // inside half range) and no rescale of O is needed.
-template <int D>
+template <int D, int NRB>
 __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ v_lane,
-                                          const f16x8 (&qrf)[D / 16], f32x16 (&acc)[D / 32], float m_run,
-                                          float& l_run) {
-  f32x16 init;
+                                          const f16x8 (&qrf)[NRB][D / 16], f32x16 (&acc)[NRB][D / 32],
+                                          const float (&m_run)[NRB], float (&l_run)[NRB]) {
+  float init[NRB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) init[r] = -m_run;
-  f32x16 sc[2];
-  qk<D>(kr_lane, qrf, init, sc);
-  float mx = sc[0][0];
+  for (int rb = 0; rb < NRB; ++rb) init[rb] = -m_run[rb];
+  f32x16 sc[NRB][2];
+  qk<D, NRB>(kr_lane, qrf, init, sc);
+  bool grow = false;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int rb = 0; rb < NRB; ++rb) {
+    float mx = sc[rb][0][0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-  mx = xhalf_max(mx);
-  if (__any(mx > 8.f)) return false;
-  float t[2][16];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
+    grow = grow || xhalf_max(mx) > 8.f;
+  }
+  if (__any(grow)) return false;
+  f16x8 pf[NRB][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[kb][r] = sc[kb][r];
-  f16x8 pf[4];
-  l_run += probs(t, pf);
-  pv<D>(v_lane, pf, acc);
+  for (int rb = 0; rb < NRB; ++rb) {
+    float t[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[kb][r] = sc[rb][kb][r];
+    l_run[rb] += probs(t, pf[rb]);
+  }
+  pv<D, NRB>(v_lane, pf, acc);
   return true;
 }
 
 // General tile (any class, optional mask) with an exact running-max update.
 // USE_R / USE_L select which logit sets the tile needs (remote / local / both
 // when it straddles the window edge); MASK adds the causal and
-// end-of-sequence mask.  Lane (r32, g) holds query qi; accumulator register r
-// of key block kb holds key j0g + kb*32 + (r/4)*8 + r%4 (j0g = tile start +
-// g*4).
-template <int D, bool USE_R, bool USE_L, bool MASK>
+// end-of-sequence mask.  Lane (r32, g) holds query qi[rb]; accumulator
+// register r of key block kb holds key j0g + kb*32 + (r/4)*8 + r%4 (j0g =
+// tile start + g*4).
+template <int D, int NRB, bool USE_R, bool USE_L, bool MASK>
 __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ kl_lane,
                                           const uint16_t* __restrict__ v_lane,
-                                          const f16x8 (&qrf)[D / 16], const f16x8 (&qlf)[D / 16],
-                                          f32x16 (&acc)[D / 32], float& m_run, float& l_run,
-                                          int qi, int j0g, int L, int w0) {
-  const f32x16 zero = {};
-  f32x16 sr[2], sl[2];
-  if constexpr (USE_R) qk<D>(kr_lane, qrf, zero, sr);
-  if constexpr (USE_L) qk<D>(kl_lane, qlf, zero, sl);
-  float t[2][16];
-  float mx = -INFINITY;
+                                          const f16x8 (&qrf)[NRB][D / 16], const f16x8 (&qlf)[NRB][D / 16],
+                                          f32x16 (&acc)[NRB][D / 32], float (&m_run)[NRB], float (&l_run)[NRB],
+                                          const int (&qi)[NRB], int j0g, int L, int w0) {
+  float zero[NRB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int rb = 0; rb < NRB; ++rb) zero[rb] = 0.f;
+  f32x16 sr[NRB][2], sl[NRB][2];
+  if constexpr (USE_R) qk<D, NRB>(kr_lane, qrf, zero, sr);
+  if constexpr (USE_L) qk<D, NRB>(kl_lane, qlf, zero, sl);
+  f16x8 pf[NRB][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kj = j0g + kb * 32 + (r >> 2) * 8 + (r & 3);
-      float s;
-      if constexpr (USE_R && USE_L) s = (qi - kj < w0) ? sl[kb][r] : sr[kb][r];
-      else if constexpr (USE_R) s = sr[kb][r];
-      else s = sl[kb][r];
-      if constexpr (MASK) s = (kj > qi || kj >= L) ? -INFINITY : s;
-      t[kb][r] = s;
-      mx = fmaxf(mx, s);
-    }
-  mx = xhalf_max(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  l_run *= alpha;
+  for (int rb = 0; rb < NRB; ++rb) {
+    float t[2][16];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-  m_run = m_new;
+      for (int r = 0; r < 16; ++r) {
+        const int kj = j0g + kb * 32 + (r >> 2) * 8 + (r & 3);
+        float s;
+        if constexpr (USE_R && USE_L) s = (qi[rb] - kj < w0) ? sl[rb][kb][r] : sr[rb][kb][r];
+        else if constexpr (USE_R) s = sr[rb][kb][r];
+        else s = sl[rb][kb][r];
+        if constexpr (MASK) s = (kj > qi[rb] || kj >= L) ? -INFINITY : s;
+        t[kb][r] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_run[rb], mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+    l_run[rb] *= alpha;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[kb][r] -= m_new;
-  f16x8 pf[4];
-  l_run += probs(t, pf);
-  pv<D>(v_lane, pf, acc);
+      for (int r = 0; r < 16; ++r) acc[rb][mb][r] *= alpha;
+    m_run[rb] = m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[kb][r] -= m_new;
+    l_run[rb] += probs(t, pf[rb]);
+  }
+  pv<D, NRB>(v_lane, pf, acc);
 }
 
-template <int D, int HPW>
-__global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
-  constexpr int RB = kWaves / HPW;  // 32-row blocks per query head
-  constexpr int ROWS = 32 * RB;     // query positions per workgroup
+template <int D, int HPW, int NRB>
+__global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
+  constexpr int NW = 8 / NRB;       // wavefronts per workgroup
+  constexpr int NT = NW * 64;       // threads per workgroup
+  constexpr int ROWS = 32 * 8 / HPW;  // query positions per workgroup
+  constexpr int WROWS = 32 * NRB;   // query positions per wavefront
   constexpr int KS = D / 16;        // k-steps of QK^T
   constexpr int MB = D / 32;        // 32-feature blocks of O^T
   constexpr int KSTR = D + 8;       // LDS row stride of key tiles (elements)
+  static_assert(NW % HPW == 0, "each wavefront owns one query head");
 
   __shared__ __attribute__((aligned(16))) uint16_t sKr[2][kBN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sKl[2][kBN * KSTR];
@@ -423,22 +490,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int64_t krow0 = key_row_offset(p.cu_k, b);
 
   const int hs = w % HPW;
-  const int rb = w / HPW;
+  const int pb = w / HPW;
   const int h = hkv * p.ratio + grp * HPW + hs;
   const int r32 = lane & 31;
   const int g = lane >> 5;
-  const int qi = i0 + rb * 32 + r32;
-  const bool qvalid = qi <= i1;
-  const int pl = qvalid ? qi : 0;
+  int qi[NRB];
+  bool qvalid[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    qi[rb] = i0 + pb * WROWS + rb * 32 + r32;
+    qvalid[rb] = qi[rb] <= i1;
+  }
 
-  // ---- query fragment rotated at f(p); the local one is built after the
-  // all-remote tiles so that it does not occupy registers during them
-  const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid ? qi - q_off : 0)) * p.Hq + h) * D;
-  f16x8 qrf[KS], qlf[KS];
-  {
+  // ---- query fragments rotated at f(p); the local ones are built after the
+  // all-remote tiles so that they do not occupy registers during them
+  f16x8 qrf[NRB][KS], qlf[NRB][KS];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int pl = qvalid[rb] ? qi[rb] : 0;
+    const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid[rb] ? qi[rb] - q_off : 0)) * p.Hq + h) * D;
     float x[KS][8];
-    load_query<D>(x, qsrc, qvalid, g);
-    rotate_query<D>(qrf, x, p.tab, pl / G, g, p.scale_log2);
+    load_query<D>(x, qsrc, qvalid[rb], g);
+    rotate_query<D>(qrf[rb], x, p.tab, pl / G, g, p.scale_log2);
   }
 
   const uint16_t* kr_base = p.kr + static_cast<int64_t>(hkv) * p.tpad * D;
@@ -447,11 +520,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int kr_off = r32 * KSTR + g * 8;
   const int v_off = r32 * kVSTR + g * 8;
 
-  float m_run = -INFINITY;  // running max (log2 domain, possibly stale by < 8)
-  float l_run = 0.f;
-  f32x16 acc[MB];
+  float m_run[NRB], l_run[NRB];  // running max (log2 domain, possibly stale by < 8), sum
+  f32x16 acc[NRB][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+  for (int rb = 0; rb < NRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x16{};
+  }
 
   const int nkt = i1 / kBN + 1;
   // tiles [0, nrem) are all-remote; classes never return to remote later
@@ -459,45 +536,43 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   while (nrem < nkt && (classify_tile(i0, i1, nrem * kBN, min(L, nrem * kBN + kBN) - 1, p.w0) & 3) == kRemote) ++nrem;
   auto cls_of = [&](int kt) { return classify_tile(i0, i1, kt * kBN, min(L, kt * kBN + kBN) - 1, p.w0); };
 
-  TileRegs tr;
+  TileRegs<D * kBN / 8 / NT> tr;
   int cls = cls_of(0);
-  load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
-  store_tile<D>(tr, sKr[0], sKl[0], sV[0], cls, tid);
+  load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
+  store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tid);
   __syncthreads();
 
   // ---- all-remote tiles: remote query only.  The inner loop is the fast
   // path; a tile it declines (first tile, a large max increase, a masked
   // tile) is redone by the slow path, which then re-enters the fast loop.
+  // The next tile's global loads are issued at the top of every iteration,
+  // before the current tile is computed, and stored to LDS after it.
   int kt = 0;
+  int ncls = 0;
   while (kt < nrem) {
     for (; kt < nrem; ++kt) {
       const int buf = kt & 1;
-      if ((cls & kDiag) || kt * kBN + kBN > L) break;
-      if (!tile_fast<D>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run)) break;
-      int ncls = 0;
+      ncls = 0;
       if (kt + 1 < nkt) {
         ncls = cls_of(kt + 1);
-        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
-        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
       }
+      if ((cls & kDiag) || kt * kBN + kBN > L) break;
+      if (!tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run)) break;
+      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       __syncthreads();
       cls = ncls;
     }
-    if (kt < nrem) {
+    if (kt < nrem) {  // the loads of tile kt + 1 are already in flight
       const int buf = kt & 1;
       const int j0g = kt * kBN + g * 4;
       if ((cls & kDiag) || kt * kBN + kBN > L)
-        tile_slow<D, true, false, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
-                                        m_run, l_run, qi, j0g, L, p.w0);
+        tile_slow<D, NRB, true, false, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
+                                             acc, m_run, l_run, qi, j0g, L, p.w0);
       else
-        tile_slow<D, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
-                                         m_run, l_run, qi, j0g, L, p.w0);
-      int ncls = 0;
-      if (kt + 1 < nkt) {
-        ncls = cls_of(kt + 1);
-        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
-        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
-      }
+        tile_slow<D, NRB, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
+                                              acc, m_run, l_run, qi, j0g, L, p.w0);
+      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       __syncthreads();
       cls = ncls;
       ++kt;
@@ -506,62 +581,71 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
   // ---- window-edge and local tiles: the local query joins (slow path)
   if (nrem < nkt) {
-    {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int pl = qvalid[rb] ? qi[rb] : 0;
+      const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid[rb] ? qi[rb] - q_off : 0)) * p.Hq + h) * D;
       float x[KS][8];
-      load_query<D>(x, qsrc, qvalid, g);
-      rotate_query<D>(qlf, x, p.tab, pl, g, p.scale_log2);
+      load_query<D>(x, qsrc, qvalid[rb], g);
+      rotate_query<D>(qlf[rb], x, p.tab, pl, g, p.scale_log2);
     }
     for (kt = nrem; kt < nkt; ++kt) {
       const int buf = kt & 1;
+      ncls = 0;
+      if (kt + 1 < nkt) {
+        ncls = cls_of(kt + 1);
+        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+      }
       const int j0g = kt * kBN + g * 4;
       const bool mask = (cls & kDiag) || kt * kBN + kBN > L;
       const uint16_t* krl = sKr[buf] + kr_off;
       const uint16_t* kll = sKl[buf] + kr_off;
       const uint16_t* vl = sV[buf] + v_off;
       if ((cls & 3) == kLocal) {
-        if (mask) tile_slow<D, false, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-        else tile_slow<D, false, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        if (mask) tile_slow<D, NRB, false, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else tile_slow<D, NRB, false, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       } else {
-        if (mask) tile_slow<D, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-        else tile_slow<D, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        if (mask) tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       }
-      int ncls = 0;
-      if (kt + 1 < nkt) {
-        ncls = cls_of(kt + 1);
-        load_tile<D>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
-        store_tile<D>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
-      }
+      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       __syncthreads();
       cls = ncls;
     }
   }
 
-  // ---- epilogue: lane holds query qi, features mb*32 + (r/4)*8 + g*4 + r%4
-  if (qvalid) {
-    const float inv = 1.f / l_run;
-    const int64_t tok = qbeg + qi - q_off;
+  // ---- epilogue: lane holds query qi[rb], features mb*32 + (r/4)*8 + g*4 + r%4
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    if (!qvalid[rb]) continue;
+    const float inv = 1.f / l_run[rb];
+    const int64_t tok = qbeg + qi[rb] - q_off;
     uint16_t* dst = p.o + (tok * p.Hq + h) * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = mb * 32 + q4 * 8 + g * 4;
-        const uint32_t w0v = pack_bf16x2(acc[mb][q4 * 4 + 0] * inv, acc[mb][q4 * 4 + 1] * inv);
-        const uint32_t w1v = pack_bf16x2(acc[mb][q4 * 4 + 2] * inv, acc[mb][q4 * 4 + 3] * inv);
+        const uint32_t w0v = pack_bf16x2(acc[rb][mb][q4 * 4 + 0] * inv, acc[rb][mb][q4 * 4 + 1] * inv);
+        const uint32_t w1v = pack_bf16x2(acc[rb][mb][q4 * 4 + 2] * inv, acc[rb][mb][q4 * 4 + 3] * inv);
         *reinterpret_cast<uint2*>(dst + d) = make_uint2(w0v, w1v);
       }
-    if (p.lse && g == 0) p.lse[static_cast<int64_t>(h) * p.total_q + tok] = (m_run + log2f(l_run)) * kLn2;
+    if (p.lse && g == 0) p.lse[static_cast<int64_t>(h) * p.total_q + tok] = (m_run[rb] + log2f(l_run[rb])) * kLn2;
   }
 }
 
 int heads_per_wg(int ratio) { return ratio % 4 == 0 ? 4 : (ratio % 2 == 0 ? 2 : 1); }
+
+// Row blocks per wavefront of the attention kernel (1: 8 waves of 32 rows;
+// 2: 4 waves of 64 rows).
+constexpr int kNRB = JL_PREFILL_NRB;
 
 template <int D, int HPW>
 hipError_t launch_attn(const Params& prm, int nqb, hipStream_t s) {
   const int units = prm.B * prm.Hkv * prm.ngroups;
   const int64_t blocks = static_cast<int64_t>(nqb) * units;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, HPW>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, prm);
+  hipLaunchKernelGGL((attn_kernel<D, HPW, kNRB>), dim3(static_cast<unsigned>(blocks)), dim3(64 * 8 / kNRB), 0, s, prm);
   return hipGetLastError();
 }
 

@@ -9,29 +9,63 @@
 namespace jl {
 
 // (cos, sin)(p * theta_k) for p in [0, npos), k in [0, D/2), theta_k =
-// theta^(-2k/D).  Angle and functions in fp64, one rounding to fp32, so the
-// table keeps full fp32 accuracy at positions near 2^17 where an fp32 angle
-// would already be off by ~1e-2 rad.  Layout: float2 tab[p * (D/2) + k].
+// theta^(-2k/D), rounded once to fp32.  Layout: float2 tab[p * (D/2) + k].
+// A thread owns one frequency and a run of kRun consecutive positions: the
+// first angle and the one-step rotation come from fp64 sincos, the rest of
+// the run from the fp64 rotation recurrence (cos, sin)(a + t) =
+// (cos a cos t - sin a sin t, sin a cos t + cos a sin t), whose error after
+// kRun steps stays near 1e-14, far below the fp32 rounding of the table.  The
+// table thus keeps full fp32 accuracy at positions near 2^17, where an fp32
+// angle would be off by ~1e-2 rad.
+//
+// With seq_L given (decode), only rows a decode can read are written: rows
+// below `remote_rows` (every remote position f(j) < w_pretrained) and each
+// sequence's local window [L_b - w0, L_b).
+constexpr int kRun = 32;
+
 __global__ void rope_table_kernel(float2* __restrict__ tab, int npos, int half, double theta,
-                                  double neg2_over_d) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<int64_t>(npos) * half) return;
-  const int p = static_cast<int>(idx / half);
-  const int k = static_cast<int>(idx % half);
+                                  double neg2_over_d, const int32_t* __restrict__ seq_L, int B,
+                                  int w0, int remote_rows) {
+  const int k = threadIdx.x % half;
+  const int run = blockIdx.x * (blockDim.x / half) + threadIdx.x / half;
+  const int p0 = run * kRun;
+  if (p0 >= npos) return;
+  const int pend = min(npos, p0 + kRun);
+  bool all = seq_L == nullptr || pend <= remote_rows;
+  if (!all) {
+    bool any = p0 < remote_rows;
+    for (int b = 0; b < B && !any; ++b) {
+      const int Lb = seq_L[b];
+      any = Lb - w0 < pend && Lb > p0;
+    }
+    if (!any) return;
+  }
   const double inv = pow(theta, neg2_over_d * k);
-  double s, c;
-  sincos(static_cast<double>(p) * inv, &s, &c);
-  tab[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
+  double s, c, s1, c1;
+  sincos(static_cast<double>(p0) * inv, &s, &c);
+  sincos(inv, &s1, &c1);
+  for (int p = p0; p < pend; ++p) {
+    bool need = all || p < remote_rows;
+    for (int b = 0; b < B && !need; ++b) need = p >= seq_L[b] - w0 && p < seq_L[b];
+    if (need) tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    const double cn = c * c1 - s * s1;
+    s = s * c1 + c * s1;
+    c = cn;
+  }
 }
 
 hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s) {
+  return launch_rope_table_rows(tab, npos, D, theta, nullptr, 0, 0, npos, s);
+}
+
+hipError_t launch_rope_table_rows(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B,
+                                  int w0, int remote_rows, hipStream_t s) {
   const int half = D / 2;
-  const int64_t n = static_cast<int64_t>(npos) * half;
-  if (n == 0) return hipSuccess;
-  const int threads = 256;
-  const int blocks = static_cast<int>((n + threads - 1) / threads);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(threads), 0, s, tab, npos, half, theta,
-                     -2.0 / static_cast<double>(D));
+  if (npos <= 0) return hipSuccess;
+  const int runs = (npos + kRun - 1) / kRun;
+  const int per_block = 256 / half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((runs + per_block - 1) / per_block), dim3(per_block * half), 0, s,
+                     tab, npos, half, theta, -2.0 / static_cast<double>(D), seq_L, B, w0, remote_rows);
   return hipGetLastError();
 }
 
