@@ -8,18 +8,24 @@
 // closer to the query than w0 is scored with classic RoPE, every other key
 // with RoPE at f(x) = floor(x / G), G from the current length L (eq. G, f).
 //
-// Kernel 1 (split): grid (splits, Hkv, B), 4 wavefronts per workgroup.  The
-// workgroup owns a contiguous key range of one sequence and one KV head; each
-// wavefront streams 16-key blocks of it and keeps its own online-softmax state
-// for all query heads of the GQA group, so every cache byte is read once.
-//   bf16: a lane loads 4 x 16 bytes of one key (A operand layout of
-//   v_mfma_f32_16x16x32_f16, rotate-half partners in the same lane), rotates
-//   them at the key's own angle (j if local, f(j) if remote) from the fp32
-//   cos/sin table, and Q K^T for the whole head group is one chain of D/32
-//   MFMAs.  The rotated operands are IEEE half (11 significant bits; bf16
-//   inputs convert exactly), accumulation fp32.  P V runs on the VALU with each lane owning D/64 features of every
-//   head; probabilities are broadcast with v_readlane.
-//   fp32: the same stream with the dot products on the VALU.
+// Kernel 1 (split).  bf16: grid (sequence x KV-head group, splits), 8
+// wavefronts per workgroup; the workgroup owns one key range of one sequence
+// for up to 8 KV heads (one wavefront per head when Hkv >= 8), so each 2 KB
+// cache row is one contiguous read and all waves share cos/sin rows.  Each
+// wavefront streams 32-key blocks and keeps its own online-softmax state for
+// all query heads of its GQA group; every cache byte is read once.
+//   * a lane loads 4 x 16 bytes of one key in the A-operand layout of
+//     v_mfma_f32_16x16x32_f16 (rotate-half partners in the same lane),
+//     rotates them at the key's own angle (j if local, f(j) if remote) from
+//     the fp32 cos/sin table, and Q K^T for the whole head group is one chain
+//     of D/32 MFMAs per 16 keys (rotated operands in IEEE half: 11
+//     significant bits, bf16 inputs convert exactly; fp32 accumulation);
+//   * the V block is staged row-major in the wavefront's own LDS slice and
+//     read back with transposing LDS reads as the B operand of
+//     v_mfma_f32_16x16x32_bf16; the probabilities stay in the registers Q K^T
+//     left them in (that is already the A-operand layout), split into a bf16
+//     high and low part so that P V keeps ~16 bits of P on exact bf16 V.
+//   fp32: the same stream with the products on the VALU (4 wavefronts).
 // Kernel 2 (combine): log-sum-exp merge of the per-wavefront partials.
 #include "jl_device.hpp"
 #include "jl_launch.hpp"
@@ -54,13 +60,217 @@ __device__ __forceinline__ float* part_ptr(const Params& p, int b, int h, int sp
 
 // ---------------------------------------------------------------- bf16
 
+// Key-block of the bf16 split kernel: 16 keys per wavefront step.
+constexpr int kKB = 16;
+
+// XOR swizzle of the 16-byte chunks of V-block row `key` (D/8 chunks per
+// row): the transposing read of 32 lanes covers 8 rows x 32 bytes, and the
+// swizzle places those 8 pieces on 8 different 32-byte bank slots of the
+// 256-byte bank space (D = 128: one row spans all of it; D = 64: rows of one
+// parity share half of it).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  if constexpr (D == 128) return (key & 7) * 2;
+  else return ((key >> 1) & 3) * 2;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, element j of lane i's result is element i % 4 of the 8 bytes
+// addressed by lane 4*j + i/4 of that group.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) const void*)p));
+}
+
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l writes lds_base + 16*l; lds_base must be
+// the same in every lane.  Counted by vmcnt like any other load.
+__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+#endif
+}
+
+// Loop-invariant state of one wavefront of the bf16 split kernel.
+template <int D>
+struct SplitCtx {
+  const uint16_t* kc;  // this (sequence, KV head)'s key rows
+  const uint16_t* vc;
+  const float2* tab;
+  const uint16_t* klane;     // kc + col*ss + g*8: this lane's K piece of block row 0
+  const uint16_t* vlane[2];  // vc + (lane/CPR)*ss + swizzled chunk, for (t*RPI) % 8 = 0 / 4
+  const f16x8* ql;     // LDS: query fragments rotated at qpos, [t][g][head]
+  uint16_t* vblk;      // LDS: this wave's V block
+  int64_t ss;
+  int qpos, kend, w0, G, col, g, lane, qcol, nr;
+  float invG;
+  int tr_addr[D / 16];  // transposed-read LDS element offsets per 16-feature block
+};
+
+// Running state: O block nb in lane (col, g) holds feature nb*16 + col of
+// heads g*4 + rr; m (log2 domain) and l of head `col`.
+template <int D>
+struct SplitState {
+  f32x4 o[D / 16];
+  float m, l;
+};
+
+// One 16-key block starting at j0 (wave-uniform).  q0 = j0 / G, r0 = j0 % G.
+// TAIL: the block may run past kend; rows are clamped to kend-1 and their
+// probabilities are zero.
+template <int D, int NR, bool TAIL>
+__device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&qrf)[D / 32],
+                                            SplitState<D>& st, int j0, int q0, int r0) {
+  constexpr int NT = D / 32;
+  constexpr int HT = NT / 2;
+  constexpr int H = D / 2;
+  constexpr int NB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;  // V rows per LDS-load instruction
+  const int col = c.col, g = c.g;
+
+  // ---- K in the A layout (lane = key j0 + col, features t*32 + g*8 ..) and
+  // the V block (row-major, chunk-swizzled) straight into LDS
+  const int jk = j0 + col;
+  const int jkr = TAIL ? min(jk, c.kend - 1) : jk;
+  // non-tail addresses: a per-lane base plus the wave-uniform row offset
+  const uint16_t* krow = TAIL ? c.kc + jkr * c.ss + g * 8 : c.klane + j0 * c.ss;
+  uint4 kr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) kr[t] = *reinterpret_cast<const uint4*>(krow + t * 32);
+#pragma unroll
+  for (int t = 0; t < kKB / RPI; ++t) {
+    const uint16_t* src;
+    if constexpr (TAIL) {
+      const int key = t * RPI + c.lane / CPR;
+      const int jv = min(j0 + key, c.kend - 1);
+      src = c.vc + jv * c.ss + ((c.lane % CPR) ^ vswz<D>(key)) * 8;
+    } else {
+      src = c.vlane[(t * RPI / 4) & 1] + (j0 + t * RPI) * c.ss;
+    }
+    load_lds16(src, c.vblk + t * 512);
+  }
+
+  // ---- rotate each key at its own angle: j if within w0 of the query,
+  // else f(j) = j / G = q0 + (r0 + col) / G.  The small quotient is exact in
+  // fp32: (n + 1/2) / G lies at least 1/(2G) from an integer and the product
+  // with the rounded reciprocal errs by under (G + 16) 2^-23 / G.  Rows past
+  // kend (tail only) read table row 0.
+  const bool klocal = c.qpos - jk < c.w0;
+  int kpos;
+  if constexpr (TAIL) {
+    kpos = jk < c.kend ? (klocal ? jk : jk / c.G) : 0;
+  } else {
+    const int frem = c.G < (1 << 20) ? q0 + static_cast<int>((static_cast<float>(r0 + col) + 0.5f) * c.invG)
+                                     : jk / c.G;
+    kpos = klocal ? jk : frem;
+  }
+  f16x8 a[NT];
+  const float4* cs4 = reinterpret_cast<const float4*>(c.tab + kpos * H + g * 8);
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
+    const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float4 cs = cs4[t * 16 + e2];  // (cos, sin) of features t*32 + g*8 + 2*e2, + 1
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int e = e2 * 2 + hh;
+        const float cc = hh ? cs.z : cs.x;
+        const float sn = hh ? cs.w : cs.y;
+        const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
+        const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
+        a[t][e] = static_cast<_Float16>(x1 * cc - x2 * sn);
+        a[t + HT][e] = static_cast<_Float16>(x2 * cc + x1 * sn);
+      }
+    }
+  }
+
+  // ---- S = K_rot Q_sel^T: lane (col = head, g) holds keys j0 + g*4 + rr
+  const bool all_remote = c.qpos - (j0 + kKB - 1) >= c.w0;
+  const bool all_local = c.qpos - j0 < c.w0;
+  f32x4 sr = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
+  if (!all_local) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qrf[t], sr, 0, 0, 0);
+  }
+  if (!all_remote) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], c.ql[(t * 4 + g) * NR + c.qcol], sl, 0, 0, 0);
+  }
+  float sv[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int j = j0 + g * 4 + rr;
+    float v = all_remote ? sr[rr] : all_local ? sl[rr] : (c.qpos - j < c.w0 ? sl[rr] : sr[rr]);
+    if (TAIL && j >= c.kend) v = -INFINITY;
+    sv[rr] = v;
+  }
+
+  // ---- online softmax with a lazy maximum: m only moves when a score
+  // exceeds it by more than 2^8 (so exp2(s - m) <= 256); O and l are
+  // rescaled then, on a wave-uniform branch
+  float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+  const bool grow = bmax > st.m + 8.f;
+  if (__any(grow)) {
+    const float m_new = grow ? bmax : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+    st.m = m_new;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float ar;
+      if constexpr (NR <= 4) ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), rr));
+      else ar = __shfl(alpha, g * 4 + rr);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) st.o[nb][rr] *= ar;
+    }
+  }
+  float pv[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) pv[rr] = __builtin_amdgcn_exp2f(sv[rr] - st.m);
+  float bsum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+  bsum += __shfl_xor(bsum, 16);
+  bsum += __shfl_xor(bsum, 32);
+  st.l += bsum;
+  // P as a bf16 high part plus a bf16 low part: on exact bf16 V the product
+  // keeps ~16 bits of P
+  const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
+  const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
+  const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+  const i16x4 phi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+  const i16x4 plo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
+
+  // ---- O += P V on MFMA (v_mfma_f32_16x16x16_bf16): A = P (head x 16
+  // keys; lane (col, g) holds keys g*4 .. g*4+3 of head col, exactly where
+  // Q K^T left them), B = V (16 keys x 16 features) from one transposing
+  // LDS read
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const i16x4 bv = lds_read_tr16(c.vblk + c.tr_addr[nb]);
+    st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.o[nb], 0, 0, 0);
+    st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.o[nb], 0, 0, 0);
+  }
+}
+
 template <int D, int NR>
-__global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
-  constexpr int NT = D / 32;    // MFMAs per block (32 features each)
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void split_bf16_kernel(Params p) {
+  constexpr int NT = D / 32;    // QK^T MFMAs per 16 keys (32 features each)
   constexpr int HT = NT / 2;    // first-half feature groups
   constexpr int H = D / 2;
-  constexpr int EPL = D / 64;   // V features per lane
+  constexpr int NB = D / 16;    // PV MFMAs per 16 keys (16 features each)
   static_assert(NR <= 16, "one MFMA column per query head");
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kWaves][kKB * D];  // per-wave V block
+  // B fragments of the query heads rotated at qpos (needed only by key
+  // blocks that reach into the local window): [wave][t][g][head]
+  __shared__ f16x8 sQl[kWaves][NT * 4 * NR];
 
   // one workgroup = one key range of one sequence for `hw` KV heads, `wph`
   // wavefronts per head: with 8 KV heads every wave streams its own 256-byte
@@ -70,7 +280,7 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
   const int b = blockIdx.x / (p.Hkv / hw);
   const int split = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = hgrp * hw + wid / p.wph;
   const int w = wid % p.wph;  // this wave's slot among the waves of its head
   const int L = p.seq_L[b];
@@ -79,15 +289,38 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
   const int qpos = L - 1;
   const int kbeg = split * p.kps;
   const int kend = min(L, kbeg + p.kps);
-  const int col = lane & 15;  // B column = query head slot; A row = key in block
-  const int g = lane >> 4;    // feature group: features t*32 + g*8 + e
 
-  const uint16_t* kc = static_cast<const uint16_t*>(p.kc) + b * p.sb + hkv * p.sh;
-  const uint16_t* vc = static_cast<const uint16_t*>(p.vc) + b * p.sb + hkv * p.sh;
+  SplitCtx<D> c;
+  c.col = lane & 15;  // QK: B column = query head slot, A row = key; PV: feature in block
+  c.g = lane >> 4;    // 16-lane group: QK feature group / PV key group
+  c.lane = lane;
+  c.kc = static_cast<const uint16_t*>(p.kc) + b * p.sb + hkv * p.sh;
+  c.vc = static_cast<const uint16_t*>(p.vc) + b * p.sb + hkv * p.sh;
+  c.tab = p.tab;
+  c.ql = sQl[wid];
+  c.vblk = sV[wid];
+  c.ss = p.ss;
+  c.qpos = qpos;
+  c.kend = kend;
+  c.w0 = p.w0;
+  c.G = G;
+  c.invG = 1.f / static_cast<float>(G);
+  c.qcol = min(c.col, NR - 1);  // columns >= NR compute unused heads
+  c.klane = c.kc + c.col * p.ss + c.g * 8;
+  {
+    // the chunk swizzle depends on the block row modulo 8 only
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = x * 4 + lane / CPR;
+      c.vlane[x] = c.vc + (lane / CPR) * p.ss + ((lane % CPR) ^ vswz<D>(key)) * 8;
+    }
+  }
+  const int col = c.col, g = c.g;
 
   // query fragments for all heads of the group, rotated at qpos and f(qpos),
   // with the softmax scale (log2 domain) folded in
-  f16x8 qlf[NT], qrf[NT];
+  f16x8 qrf[NT];
   {
     float x[NT][8];
     if (col < p.ratio) {
@@ -107,7 +340,8 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
         for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
     }
     const int fq = qpos / G;
-    const float c = p.scale_log2;
+    const float sc = p.scale_log2;
+    f16x8 ql[NT];
 #pragma unroll
     for (int t = 0; t < HT; ++t)
 #pragma unroll
@@ -116,140 +350,63 @@ __global__ __launch_bounds__(kWaves * 64) void split_bf16_kernel(Params p) {
         const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
         const float2 cr = p.tab[static_cast<int64_t>(fq) * H + kk];
         const float x1 = x[t][e], x2 = x[t + HT][e];
-        qlf[t][e] = static_cast<_Float16>((x1 * cl.x - x2 * cl.y) * c);
-        qlf[t + HT][e] = static_cast<_Float16>((x2 * cl.x + x1 * cl.y) * c);
-        qrf[t][e] = static_cast<_Float16>((x1 * cr.x - x2 * cr.y) * c);
-        qrf[t + HT][e] = static_cast<_Float16>((x2 * cr.x + x1 * cr.y) * c);
+        ql[t][e] = static_cast<_Float16>((x1 * cl.x - x2 * cl.y) * sc);
+        ql[t + HT][e] = static_cast<_Float16>((x2 * cl.x + x1 * cl.y) * sc);
+        qrf[t][e] = static_cast<_Float16>((x1 * cr.x - x2 * cr.y) * sc);
+        qrf[t + HT][e] = static_cast<_Float16>((x2 * cr.x + x1 * cr.y) * sc);
       }
-  }
-
-  float m_run = -INFINITY;  // lanes with col = head slot carry that head's state
-  float l_run = 0.f;
-  float oacc[NR][EPL];
+    if (col < NR) {
 #pragma unroll
-  for (int hh = 0; hh < NR; ++hh)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) oacc[hh][e] = 0.f;
-
-  const int step = p.wph * kBlk;
-  for (int j0 = kbeg + w * kBlk; j0 < kend; j0 += step) {
-    // ---- stream K (A layout: lane = key j0 + col, features t*32 + g*8 ..)
-    // and V (lane = features lane*EPL .. of each of the 16 keys)
-    uint4 kr[NT];
-    uint32_t vr[kBlk];
-    {
-      const int jk = j0 + col;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        kr[t] = jk < kend ? *reinterpret_cast<const uint4*>(kc + jk * p.ss + t * 32 + g * 8) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < kBlk; ++m) {
-        const int jv = j0 + m;
-        if constexpr (EPL == 2)
-          vr[m] = jv < kend ? *reinterpret_cast<const uint32_t*>(vc + jv * p.ss + lane * 2) : 0u;
-        else
-          vr[m] = jv < kend ? static_cast<uint32_t>(vc[jv * p.ss + lane]) : 0u;
-      }
-    }
-
-    // ---- rotate each key at its own angle (registers only; cache untouched)
-    const int jk = j0 + col;
-    const bool kval = jk < kend;
-    const bool klocal = qpos - jk < p.w0;
-    const int kpos = kval ? (klocal ? jk : jk / G) : 0;
-    f16x8 a[NT];
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
-      const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
-      const float4* cs4 = reinterpret_cast<const float4*>(p.tab + static_cast<int64_t>(kpos) * H + t * 32 + g * 8);
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float4 cs = cs4[e2];  // (cos, sin) of features 2*e2 and 2*e2 + 1
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int e = e2 * 2 + hh;
-          const float cc = hh ? cs.z : cs.x;
-          const float ss = hh ? cs.w : cs.y;
-          const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
-          const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
-          a[t][e] = static_cast<_Float16>(x1 * cc - x2 * ss);
-          a[t + HT][e] = static_cast<_Float16>(x2 * cc + x1 * ss);
-        }
-      }
-    }
-
-    // ---- S = K_rot Q_sel^T: lane (col = head, g) holds keys j0 + g*4 + rr
-    const bool all_remote = qpos - (j0 + kBlk - 1) >= p.w0;
-    const bool all_local = qpos - j0 < p.w0;
-    f32x4 sr = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
-    if (!all_local) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qrf[t], sr, 0, 0, 0);
-    }
-    if (!all_remote) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qlf[t], sl, 0, 0, 0);
-    }
-    float s[4];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j = j0 + g * 4 + rr;
-      float v = (qpos - j < p.w0) ? sl[rr] : sr[rr];
-      v = j < kend ? v : -INFINITY;
-      s[rr] = v;
-      bmax = fmaxf(bmax, v);
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float bsum = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      s[rr] = __builtin_amdgcn_exp2f(s[rr] - m_new);
-      bsum += s[rr];
-    }
-    bsum += __shfl_xor(bsum, 16);
-    bsum += __shfl_xor(bsum, 32);
-    l_run = l_run * alpha + bsum;
-    m_run = m_new;
-
-    // ---- O += P V on the VALU; p(key m, head hh) lives in lane (m/4)*16 + hh, reg m%4
-#pragma unroll
-    for (int hh = 0; hh < NR; ++hh) {
-      const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh));
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) oacc[hh][e] *= al;
-    }
-#pragma unroll
-    for (int m = 0; m < kBlk; ++m) {
-      float vf[EPL];
-      vf[0] = __uint_as_float(vr[m] << 16);
-      if constexpr (EPL == 2) vf[1] = __uint_as_float(vr[m] & 0xffff0000u);
-#pragma unroll
-      for (int hh = 0; hh < NR; ++hh) {
-        const float pm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[m & 3]), (m >> 2) * 16 + hh));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) oacc[hh][e] = fmaf(pm, vf[e], oacc[hh][e]);
-      }
+      for (int t = 0; t < NT; ++t) sQl[wid][(t * 4 + g) * NR + col] = ql[t];
     }
   }
 
-  // ---- this wavefront's partial state for every head of the group
+  // transposed-read address of lane (g, col): the 4 features nb*16 +
+  // 4*(col%4) .. of key g*4 + col/4; 16-byte chunk ch of a row sits at
+  // position ch ^ vswz(row)
+  {
+    const int tr_row = g * 4 + (col >> 2);
+    const int tr_half = (col & 1) * 4;
+    const int tr_c = (col >> 1) & 1;
+    const int tr_x = vswz<D>(tr_row);
 #pragma unroll
-  for (int hh = 0; hh < NR; ++hh) {
-    if (hh >= p.ratio) break;
-    float* dst = part_ptr<D>(p, b, hkv * p.ratio + hh, split, w);
+    for (int nb = 0; nb < NB; ++nb) c.tr_addr[nb] = tr_row * D + ((nb * 2 + tr_c) ^ tr_x) * 8 + tr_half;
+  }
+
+  SplitState<D> st;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[lane * EPL + e] = oacc[hh][e];
-    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), hh));
-    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), hh));
-    if (lane == 0) {
-      dst[D] = mh;
-      dst[D + 1] = lh;
+  for (int nb = 0; nb < NB; ++nb) st.o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  // blocks j0 = kbeg + w*16 + n*step; j0 / G tracked as quotient + remainder
+  const int step = p.wph * kKB;
+  const int qs = step / G, rs = step % G;
+  int j0 = kbeg + w * kKB;
+  int q0 = j0 / G, r0 = j0 % G;
+  for (; j0 + kKB <= kend; j0 += step) {
+    split_block<D, NR, false>(c, qrf, st, j0, q0, r0);
+    q0 += qs;
+    r0 += rs;
+    if (r0 >= G) { r0 -= G; ++q0; }
+  }
+  if (j0 < kend) split_block<D, NR, true>(c, qrf, st, j0, q0, r0);
+
+  // ---- this wavefront's partial state: O feature nb*16 + col of head
+  // g*4 + rr in register rr; m and l of head hh in lane hh
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int hh = g * 4 + rr;
+    if (hh < p.ratio) {
+      float* dst = part_ptr<D>(p, b, hkv * p.ratio + hh, split, w);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dst[nb * 16 + col] = st.o[nb][rr];
     }
+  }
+  if (g == 0 && col < p.ratio) {
+    float* dst = part_ptr<D>(p, b, hkv * p.ratio + col, split, w);
+    dst[D] = st.m;
+    dst[D + 1] = st.l;
   }
 }
 
@@ -461,15 +618,15 @@ int keys_per_split(int max_L, int nsplit) {
 
 }  // namespace
 
-// Key-range splits per (sequence, KV head): about 8192 streaming wavefronts
-// in all (two per SIMD slot at the split kernel's occupancy), each split at
-// least 256 keys, and at most 128 splits (the combine merges up to 1024
-// partial states).
+// Key-range splits per (sequence, KV head): about 16384 streaming
+// wavefronts in all (four per slot at the split kernel's 4 waves per SIMD),
+// each split at least 256 keys, and at most 128 splits (the combine merges up
+// to 1024 partial states).
 int decode_num_splits(int B, int max_L, int Hkv) {
   int hw = 1;
   while (hw < kWaves && Hkv % (hw * 2) == 0) hw *= 2;
   const int64_t waves = static_cast<int64_t>(B) * Hkv * (kWaves / hw);
-  int64_t ns = (8192 + waves - 1) / waves;
+  int64_t ns = (16384 + waves - 1) / waves;
   const int64_t cap = (static_cast<int64_t>(max_L) + 255) / 256;
   if (ns > cap) ns = cap;
   if (ns > 128) ns = 128;

@@ -27,16 +27,16 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even (inputs here are finite).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(float_to_bf16_bits(lo)) |
-         (static_cast<uint32_t>(float_to_bf16_bits(hi)) << 16);
+  const bf16x2v h = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Two floats -> packed IEEE half (round to nearest even).
