@@ -156,13 +156,6 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 
 constexpr int kVSTR = kBN + 8;  // LDS row stride of V^T tiles (elements, 16-byte rows)
 
-#ifndef JL_PIN_SCHEDULE
-#define JL_PIN_SCHEDULE 0
-#endif
-// Pin an LDS read-ahead order on the MFMA loops (measured: no gain at one
-// row block per wave, so off by default).
-constexpr bool kPinSchedule = JL_PIN_SCHEDULE != 0;
-
 // chunk c of a key tile: row c / (D/8), 16-byte column c % (D/8)
 template <int D>
 __device__ __forceinline__ uint4 ld_k(const uint16_t* base, int64_t row0, int c) {
@@ -293,24 +286,19 @@ __device__ __forceinline__ void pv(const uint16_t* __restrict__ v_lane, const f1
                                    f32x16 (&acc)[NRB][D / 32]) {
   constexpr int MB = D / 32;
   constexpr int NF = 4 * MB;  // fragments: (k-step, feature block), feature block fastest
-  constexpr int PF = 4;
-  f16x8 a[NF];
+  constexpr int PF = 4;       // fragments read ahead of the MFMAs (measured best of 4 / 8 / all)
+  f16x8 a[PF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int f = 0; f < PF; ++f)
     a[f] = *reinterpret_cast<const f16x8*>(v_lane + (f % MB) * 32 * kVSTR + (f / MB) * 16);
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int f = 0; f < NF; ++f) {
+    const f16x8 cur = a[f % PF];
+    if (f + PF < NF)
+      a[f % PF] = *reinterpret_cast<const f16x8*>(v_lane + ((f + PF) % MB) * 32 * kVSTR + ((f + PF) / MB) * 16);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
-      acc[rb][f % MB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], pf[rb][f / MB], acc[rb][f % MB], 0, 0, 0);
-  if constexpr (kPinSchedule) {
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int f = 0; f < NF - PF; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
+      acc[rb][f % MB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, pf[rb][f / MB], acc[rb][f % MB], 0, 0, 0);
   }
 }
 
@@ -324,31 +312,24 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
   constexpr int KSTR = D + 8;
   constexpr int KS = D / 16;
   constexpr int NF = 2 * KS;  // fragments per tile: (key block, k-step)
-  constexpr int PF = 4;
+  constexpr int PF = 4;       // fragments read ahead of the MFMAs (measured best of 4 / 8 / all)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[rb][kb][r] = init[rb];
-  f16x8 a[NF];
+  f16x8 a[PF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
-    a[f] = *reinterpret_cast<const f16x8*>(k_lane + (f & 1) * 32 * KSTR + (f >> 1) * 16);
+  for (int f = 0; f < PF; ++f) a[f] = *reinterpret_cast<const f16x8*>(k_lane + (f & 1) * 32 * KSTR + (f >> 1) * 16);
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int f = 0; f < NF; ++f) {
+    const f16x8 cur = a[f % PF];
+    if (f + PF < NF)
+      a[f % PF] = *reinterpret_cast<const f16x8*>(k_lane + ((f + PF) & 1) * 32 * KSTR + ((f + PF) >> 1) * 16);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
-      sc[rb][f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], qf[rb][f >> 1], sc[rb][f & 1], 0, 0, 0);
-  // schedule: PF reads, then (NRB MFMAs, one read) until the reads run out
-  if constexpr (kPinSchedule) {
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int f = 0; f < NF - PF; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
+      sc[rb][f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, qf[rb][f >> 1], sc[rb][f & 1], 0, 0, 0);
   }
 }
 
