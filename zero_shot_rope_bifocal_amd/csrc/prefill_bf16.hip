@@ -333,7 +333,8 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
   }
 }
 
-// Fast path of an all-remote, unmasked tile.  The score accumulators start at
+// Fast path of an unmasked tile scored with one rotation (all-remote, or
+// all-local with the local rotations).  The score accumulators start at
 // -m_run, so they come out relative to the running max.  If any row's max
 // rose by more than 8 (log2) the tile is left to the slow path and nothing is
 // changed; otherwise the stale max stands (probabilities stay below 2^8, far
@@ -570,7 +571,10 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       load_query<D>(x, qsrc, qvalid[rb], g);
       rotate_query<D>(qlf[rb], x, p.tab, pl, g, p.scale_log2);
     }
-    for (kt = nrem; kt < nkt; ++kt) {
+    // window-edge tiles need both logit sets
+    int nloc = nrem;
+    while (nloc < nkt && (cls_of(nloc) & 3) != kLocal) ++nloc;
+    for (kt = nrem; kt < nloc; ++kt) {
       const int buf = kt & 1;
       ncls = 0;
       if (kt + 1 < nkt) {
@@ -578,20 +582,48 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
       }
       const int j0g = kt * kBN + g * 4;
-      const bool mask = (cls & kDiag) || kt * kBN + kBN > L;
       const uint16_t* krl = sKr[buf] + kr_off;
       const uint16_t* kll = sKl[buf] + kr_off;
       const uint16_t* vl = sV[buf] + v_off;
-      if ((cls & 3) == kLocal) {
-        if (mask) tile_slow<D, NRB, false, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-        else tile_slow<D, NRB, false, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-      } else {
-        if (mask) tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-        else tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-      }
+      if ((cls & kDiag) || kt * kBN + kBN > L)
+        tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+      else
+        tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       __syncthreads();
       cls = ncls;
+    }
+    // all-local tiles: one rotation again, so the fast path as for the
+    // remote tiles (only the local query is live from here on)
+    while (kt < nkt) {
+      for (; kt < nkt; ++kt) {
+        const int buf = kt & 1;
+        ncls = 0;
+        if (kt + 1 < nkt) {
+          ncls = cls_of(kt + 1);
+          load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls,
+                           tid);
+        }
+        if ((cls & kDiag) || kt * kBN + kBN > L) break;
+        if (!tile_fast<D, NRB>(sKl[buf] + kr_off, sV[buf] + v_off, qlf, acc, m_run, l_run)) break;
+        if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+        __syncthreads();
+        cls = ncls;
+      }
+      if (kt < nkt) {  // the loads of tile kt + 1 are already in flight
+        const int buf = kt & 1;
+        const int j0g = kt * kBN + g * 4;
+        if ((cls & kDiag) || kt * kBN + kBN > L)
+          tile_slow<D, NRB, false, true, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
+                                               acc, m_run, l_run, qi, j0g, L, p.w0);
+        else
+          tile_slow<D, NRB, false, true, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
+                                                acc, m_run, l_run, qi, j0g, L, p.w0);
+        if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+        __syncthreads();
+        cls = ncls;
+        ++kt;
+      }
     }
   }
 
