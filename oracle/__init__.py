@@ -5,4 +5,5 @@ from .bifocal import (  # noqa: F401
     group_size, remote_positions, rope_frequencies, rope_rotate,
     bifocal_sequence, bifocal_prefill, bifocal_rows, bifocal_decode,
     bifocal_sequence_ie, masked_attention, correction_rotation, tile_classes,
+    bifocal_sequence_prerotated, bifocal_decode_prerotated,
 )

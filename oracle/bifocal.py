@@ -267,6 +267,71 @@ def correction_rotation(x_rot, positions, G: int, theta: float):
     return rope_rotate(x_rot, remote_positions(p, G) - p, theta)
 
 
+def bifocal_sequence_prerotated(q_rot, k_rot, v, q_pos, L: int, w_pretrained: int,
+                                w0: int, theta: float, scale: float | None = None):
+    """Bifocal attention of one sequence whose queries and keys arrive already
+    rotated at their true positions (q_rot = R(p_i) q, k_rot = R(p_j) k, the
+    usual RoPE cache).  Local logits are q_rot . k_rot as stored; remote
+    logits use the correction rotation R(f(p) - p) on both sides ("On-the-Fly
+    Correction Rotation"), so the stored vectors are never rewritten.  Same
+    arguments and returns as bifocal_sequence, fp64, mask-select."""
+    q_rot = np.asarray(q_rot, dtype=np.float64)
+    k_rot = np.asarray(k_rot, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    n, Hq, d = q_rot.shape
+    Hkv = k_rot.shape[1]
+    if k_rot.shape[0] != L or v.shape[0] != L:
+        raise ValueError("k and v must hold L rows")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if n and (q_pos.min() < 0 or q_pos.max() >= L):
+        raise ValueError("query positions must lie in [0, L)")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = group_size(L, w_pretrained)
+    kpos = np.arange(L, dtype=np.int64)
+    rep = Hq // Hkv
+    out = np.zeros((n, Hq, v.shape[2]), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    for hk in range(Hkv):
+        kl = k_rot[:, hk]                                  # as stored
+        kr = correction_rotation(k_rot[:, hk], kpos, G, theta)
+        vals = v[:, hk]
+        for h in range(hk * rep, (hk + 1) * rep):
+            ql = q_rot[:, h]
+            qr = correction_rotation(q_rot[:, h], q_pos, G, theta)
+            blk = _row_block(L)
+            for r0 in range(0, n, blk):
+                r1 = min(n, r0 + blk)
+                gap = q_pos[r0:r1, None] - kpos[None, :]         # causal distance
+                logit = np.where(gap >= w0, scale * (qr[r0:r1] @ kr.T), scale * (ql[r0:r1] @ kl.T))
+                logit[gap < 0] = -np.inf
+                top = logit.max(axis=1, keepdims=True)
+                wgt = np.exp(logit - top)
+                z = wgt.sum(axis=1, keepdims=True)
+                out[r0:r1, h] = (wgt @ vals) / z
+                lse[r0:r1, h] = top[:, 0] + np.log(z[:, 0])
+    return out, lse
+
+
+def bifocal_decode_prerotated(q_rot, k_cache_rot, v_cache, seq_L, w_pretrained: int,
+                              w0: int, theta: float, scale: float | None = None):
+    """Decode over a pre-rotated cache (see bifocal_sequence_prerotated); the
+    new query, rotated at its position seq_L[b] - 1, is q_rot[b]."""
+    q_rot = np.asarray(q_rot)
+    B, Hq, _ = q_rot.shape
+    out = np.zeros((B, Hq, np.asarray(v_cache).shape[3]), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_L[b])
+        o, s = bifocal_sequence_prerotated(q_rot[b:b + 1], k_cache_rot[b, :L], v_cache[b, :L],
+                                           [L - 1], L, w_pretrained, w0, theta, scale)
+        out[b] = o[0]
+        lse[b] = s[0]
+    return out, lse
+
+
 def tile_classes(Lq: int, L: int, q_offset: int, w0: int, BM: int, BN: int):
     """Class of every (query block, key tile) of one sequence, decided pair by
     pair.  Query rows are positions q_offset .. q_offset+Lq-1 in blocks of BM

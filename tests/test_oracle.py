@@ -229,6 +229,56 @@ def test_inclusion_exclusion_identity(L, wp, w0):
     assert np.max(np.abs(lse - lse2)) < 1e-10
 
 
+PREROT_CASES = [
+    # (L, d, Hq, Hkv, wp, w0, theta)
+    (40, 8, 4, 2, 8, 6, 1e4),       # G = 5, straddling window
+    (33, 16, 2, 1, 33, 5, 1e4),     # G = 1
+    (29, 8, 2, 2, 4, 0, 100.0),     # w0 = 0: all remote
+    (25, 4, 2, 1, 3, 30, 1e6),      # w0 >= L: all local
+]
+
+
+@pytest.mark.parametrize("case", PREROT_CASES)
+def test_prerotated_cache_matches_raw_inputs(case):
+    """Queries and keys handed over already rotated at their true positions
+    (the usual RoPE cache) give the bifocal result of the raw vectors: the
+    correction rotation R(f(p) - p) composes with R(p) to R(f(p))."""
+    L, d, Hq, Hkv, wp, w0, theta = case
+    rng = np.random.default_rng(L * 31 + d)
+    q, k, v = _rand(rng, L, Hq, d), _rand(rng, L, Hkv, d), _rand(rng, L, Hkv, d)
+    pos = np.arange(L)
+    q_rot = np.stack([complex_rope(q[:, h], pos, theta) for h in range(Hq)], axis=1)
+    k_rot = np.stack([complex_rope(k[:, h], pos, theta) for h in range(Hkv)], axis=1)
+    o1, l1 = oracle.bifocal_sequence_prerotated(q_rot, k_rot, v, pos, L, wp, w0, theta)
+    o2, l2 = brute_bifocal(q, k, v, pos, L, wp, w0, theta)
+    assert np.max(np.abs(o1 - o2)) < 1e-10
+    assert np.max(np.abs(l1 - l2)) < 1e-10
+
+
+def test_prerotated_wide_window_is_plain_attention():
+    """w0 >= L over a pre-rotated cache: textbook causal softmax attention of
+    the stored vectors, no rotation at all."""
+    rng = np.random.default_rng(8)
+    L, d = 21, 8
+    q, k, v = _rand(rng, L, 2, d), _rand(rng, L, 1, d), _rand(rng, L, 1, d)
+    o, lse = oracle.bifocal_sequence_prerotated(q, k, v, np.arange(L), L, 4, L, 1e4)
+    for h in range(2):
+        s = (q[:, h] @ k[:, 0].T) / math.sqrt(d)
+        s[np.triu_indices(L, 1)] = -np.inf
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        ref = (w @ v[:, 0]) / w.sum(axis=1, keepdims=True)
+        assert np.max(np.abs(o[:, h] - ref)) < 1e-12
+
+
+def test_prerotated_decode_is_last_row():
+    rng = np.random.default_rng(9)
+    L, d = 30, 8
+    q, k, v = _rand(rng, L, 4, d), _rand(rng, L, 2, d), _rand(rng, L, 2, d)
+    full, _ = oracle.bifocal_sequence_prerotated(q, k, v, np.arange(L), L, 7, 4, 1e4)
+    dec, _ = oracle.bifocal_decode_prerotated(q[L - 1:L], k[None], v[None], [L], 7, 4, 1e4)
+    assert np.max(np.abs(dec[0] - full[L - 1])) < 1e-12
+
+
 def test_decode_is_last_prefill_row():
     rng = np.random.default_rng(7)
     B, S, Hq, Hkv, d = 3, 40, 4, 2, 16
