@@ -131,6 +131,35 @@ int jl_bifocal_prefill_attend(const void* q, const void* k, const void* v, void*
                               double rope_theta, float softmax_scale, const void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Flag bits of the *_ex entry points. */
+enum { JL_FLAG_PREROTATED = 1 };
+
+/* The same prefill calls with flags.  JL_FLAG_PREROTATED: q and k arrive
+ * already rotated at their true positions (R(p) q, R(p) k: the usual RoPE
+ * cache layout), everything else as above.  Local pairs are then scored on
+ * the stored vectors as they are; remote pairs apply the correction rotation
+ * R(f(p) - p) to both sides on the fly ("Inference Efficiency Mechanisms",
+ * correction rotation; "Dynamic Bifocal RoPE", eq. f), and the inputs stay
+ * untouched.  A workspace prepared with the flag must be attended with it.
+ * Unknown flag bits: JL_ERR_INVALID_ARG.  flags = 0 is exactly the call
+ * without _ex. */
+int jl_bifocal_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                          int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                          double rope_theta, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream, unsigned flags);
+int jl_bifocal_prefill_prepare_ex(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
+                                  int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
+                                  int w_pretrained, double rope_theta, void* workspace,
+                                  size_t workspace_bytes, void* stream, unsigned flags);
+int jl_bifocal_prefill_attend_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                                 int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                                 double rope_theta, float softmax_scale, const void* workspace,
+                                 size_t workspace_bytes, void* stream, unsigned flags);
+
 /* Bytes of device workspace jl_bifocal_decode needs, or 0 on invalid sizes. */
 size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv,
                                         int head_dim);
@@ -155,6 +184,19 @@ int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache,
                       int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
                       double rope_theta, float softmax_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* jl_bifocal_decode with flags.  JL_FLAG_PREROTATED: q holds R(L-1) q and the
+ * key cache holds R(j) k_j (keys rotated at their absolute positions, the
+ * cache layout the pages keep); local keys are used as stored and remote keys
+ * get the correction rotation R(f(j) - j) in registers as they stream by, so
+ * the cache is never rewritten ("Inference Efficiency Mechanisms").  flags =
+ * 0 is exactly jl_bifocal_decode. */
+int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                         int64_t stride_b, int64_t stride_s, int64_t stride_h,
+                         void* o, float* lse, int dtype, const int32_t* seq_L, int B, int max_L,
+                         int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                         double rope_theta, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream, unsigned flags);
 
 /* Integer position map of a packed batch, exactly as the prefill kernels use
  * it (eq. G, eq. f).  Device outputs: pos_out/f_out int32 [total_q] (query

@@ -113,3 +113,14 @@ def test_status_strings():
     for c in (0, -1, -2, -3, -4):
         assert L.jl_status_string(c)
     assert jl.version().count(".") == 2
+
+
+def test_unknown_flags_rejected():
+    """The *_ex entry points reject flag bits they do not know before any HIP
+    call (null pointers would otherwise be the first complaint)."""
+    L = _lib()
+    rc = L.jl_bifocal_decode_ex(None, None, None, 0, 0, 0, None, None, 1, None, 1, 1, 1, 1, 128, 1, 0, 1e4,
+                                0.0, None, 0, None, 2)
+    assert rc == -1 and b"flag" in L.jl_last_error()
+    rc = L.jl_bifocal_prefill_prepare_ex(None, None, 1, None, 1, 1, 1, 1, 128, 1, 1e4, None, 0, None, 8)
+    assert rc == -1 and b"flag" in L.jl_last_error()

@@ -15,12 +15,13 @@ import ctypes
 import os
 
 __all__ = [
-    "JL_F32", "JL_BF16", "JetLongError", "library_path", "lib",
+    "JL_F32", "JL_BF16", "JL_FLAG_PREROTATED", "JetLongError", "library_path", "lib",
     "group_size", "prefill", "prefill_prepare", "prefill_attend", "decode", "prefill_workspace_size", "decode_workspace_size",
     "remote_positions", "tile_classes", "prefill_tile_shape", "version",
 ]
 
 JL_F32, JL_BF16 = 0, 1
+JL_FLAG_PREROTATED = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -62,6 +63,15 @@ def lib() -> ctypes.CDLL:
     L.jl_bifocal_decode.argtypes = ([c_vp] * 3 + [c_i64] * 3 + [c_vp, c_vp, c_int, c_vp] +
                                     [c_int] * 7 + [c_d, c_f, c_vp, c_sz, c_vp])
     L.jl_bifocal_decode.restype = c_int
+    c_u = ctypes.c_uint
+    L.jl_bifocal_prefill_ex.argtypes = L.jl_bifocal_prefill.argtypes + [c_u]
+    L.jl_bifocal_prefill_ex.restype = c_int
+    L.jl_bifocal_prefill_prepare_ex.argtypes = L.jl_bifocal_prefill_prepare.argtypes + [c_u]
+    L.jl_bifocal_prefill_prepare_ex.restype = c_int
+    L.jl_bifocal_prefill_attend_ex.argtypes = L.jl_bifocal_prefill_attend.argtypes + [c_u]
+    L.jl_bifocal_prefill_attend_ex.restype = c_int
+    L.jl_bifocal_decode_ex.argtypes = L.jl_bifocal_decode.argtypes + [c_u]
+    L.jl_bifocal_decode_ex.restype = c_int
     L.jl_bifocal_remote_positions.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     L.jl_bifocal_remote_positions.restype = c_int
     L.jl_bifocal_tile_classes.argtypes = [c_int] * 5 + [c_vp, c_vp]
@@ -137,11 +147,12 @@ def decode_workspace_size(dtype: int, B: int, max_L: int, Hq: int, Hkv: int, hea
 
 def prefill(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int, rope_theta: float,
             cu_seqlens_k=None, max_seqlen_k: int | None = None, softmax_scale: float = 0.0,
-            out=None, lse=None, workspace=None, return_lse: bool = False):
+            out=None, lse=None, workspace=None, return_lse: bool = False, prerotated: bool = False):
     """Packed varlen bifocal prefill.  q [Tq, Hq, d], k/v [Tk, Hkv, d] (cuda,
     float32 or bfloat16, contiguous); cu_seqlens int32 cuda [B+1].  Queries of
-    sequence b sit at its last Lq_b positions.  Returns out (and lse [Hq, Tq]
-    float32 when asked)."""
+    sequence b sit at its last Lq_b positions.  prerotated: q and k hold
+    R(p) q, R(p) k (a RoPE cache).  Returns out (and lse [Hq, Tq] float32 when
+    asked)."""
     torch = _torch()
     _need_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
     for t in (q, k, v):
@@ -166,16 +177,17 @@ def prefill(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int
     need = prefill_workspace_size(dt, B, Tk, max_seqlen_k, Hq, Hkv, d)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    code = lib().jl_bifocal_prefill(
+    code = lib().jl_bifocal_prefill_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), dt, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, int(w_pretrained), int(w0),
-        float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device))
+        float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device),
+        JL_FLAG_PREROTATED if prerotated else 0)
     _check(code)
     return (out, lse) if return_lse else out
 
 
 def prefill_prepare(k, v, cu_seqlens_k, max_seqlen_k: int, w_pretrained: int, rope_theta: float,
-                    Hq: int | None = None, workspace=None):
+                    Hq: int | None = None, workspace=None, prerotated: bool = False):
     """First stage of ``prefill``: fills and returns a workspace holding the
     cos/sin table and (bf16) the rotated keys and transposed values."""
     torch = _torch()
@@ -188,17 +200,19 @@ def prefill_prepare(k, v, cu_seqlens_k, max_seqlen_k: int, w_pretrained: int, ro
     need = prefill_workspace_size(dt, B, Tk, max_seqlen_k, Hq or Hkv, Hkv, d)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
-    _check(lib().jl_bifocal_prefill_prepare(_ptr(k), _ptr(v), dt, _ptr(cu_seqlens_k), B, Tk, int(max_seqlen_k),
-                                            Hkv, d, int(w_pretrained), float(rope_theta), _ptr(workspace),
-                                            workspace.numel(), _stream(k.device)))
+    _check(lib().jl_bifocal_prefill_prepare_ex(_ptr(k), _ptr(v), dt, _ptr(cu_seqlens_k), B, Tk, int(max_seqlen_k),
+                                               Hkv, d, int(w_pretrained), float(rope_theta), _ptr(workspace),
+                                               workspace.numel(), _stream(k.device),
+                                               JL_FLAG_PREROTATED if prerotated else 0))
     return workspace
 
 
 def prefill_attend(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int,
                    rope_theta: float, workspace, cu_seqlens_k=None, max_seqlen_k: int | None = None,
-                   softmax_scale: float = 0.0, out=None, lse=None, return_lse: bool = False):
+                   softmax_scale: float = 0.0, out=None, lse=None, return_lse: bool = False,
+                   prerotated: bool = False):
     """Second stage of ``prefill`` over a workspace from ``prefill_prepare``
-    made with the same keys, values and key-side arguments."""
+    made with the same keys, values, key-side arguments and ``prerotated``."""
     torch = _torch()
     _need_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, workspace)
     dt = _dtype_code(q)
@@ -211,19 +225,21 @@ def prefill_attend(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, 
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
-    _check(lib().jl_bifocal_prefill_attend(
+    _check(lib().jl_bifocal_prefill_attend_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), dt, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, int(w_pretrained), int(w0),
-        float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device)))
+        float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device),
+        JL_FLAG_PREROTATED if prerotated else 0))
     return (out, lse) if return_lse else out
 
 
 def decode(q, k_cache, v_cache, seq_L, w_pretrained: int, w0: int, rope_theta: float,
            max_L: int | None = None, softmax_scale: float = 0.0, out=None, lse=None, workspace=None,
-           return_lse: bool = False):
+           return_lse: bool = False, prerotated: bool = False):
     """One query per sequence against an untouched cache.  q [B, Hq, d];
     caches [B, S_max, Hkv, d] with d contiguous (any strides on the other
-    axes, same for both); seq_L int32 cuda [B] counts the new token."""
+    axes, same for both); seq_L int32 cuda [B] counts the new token.
+    prerotated: q and the key cache hold vectors rotated at their positions."""
     torch = _torch()
     _need_cuda(q, k_cache, v_cache, seq_L)
     if seq_L.dtype != torch.int32:
@@ -245,10 +261,11 @@ def decode(q, k_cache, v_cache, seq_L, w_pretrained: int, w0: int, rope_theta: f
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     sb, ss, sh, _ = k_cache.stride()
-    code = lib().jl_bifocal_decode(
+    code = lib().jl_bifocal_decode_ex(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), sb, ss, sh, _ptr(out), _ptr(lse), dt, _ptr(seq_L),
         B, int(max_L), Hq, Hkv, d, int(w_pretrained), int(w0), float(rope_theta),
-        float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device))
+        float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device),
+        JL_FLAG_PREROTATED if prerotated else 0)
     _check(code)
     return (out, lse) if return_lse else out
 

@@ -112,17 +112,19 @@ int prefill_args(const void* q, const void* k, const void* v, void* o, float* ls
 
 extern "C" {
 
-int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
-                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
-                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
-                       int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
-                       float softmax_scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+int jl_bifocal_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                          int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                          int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
+                          float softmax_scale, void* workspace, size_t workspace_bytes,
+                          void* stream, unsigned flags) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   jl::PrefillCall c;
   const int st = prefill_args(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
                               max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
                               rope_theta, softmax_scale, workspace, workspace_bytes, &c);
   if (st != JL_OK || c.B == 0) return st;
+  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_prepare(c, s) : jl::launch_prefill_f32_prepare(c, s);
   if (e != hipSuccess) return hip_status(e, "jl_bifocal_prefill prepare launch");
@@ -130,10 +132,11 @@ int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, flo
   return hip_status(e, "jl_bifocal_prefill attend launch");
 }
 
-int jl_bifocal_prefill_prepare(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
-                               int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
-                               int w_pretrained, double rope_theta, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+int jl_bifocal_prefill_prepare_ex(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
+                                  int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
+                                  int w_pretrained, double rope_theta, void* workspace,
+                                  size_t workspace_bytes, void* stream, unsigned flags) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   int st = check_common(dtype, Hkv, Hkv, head_dim, w_pretrained, 0, rope_theta, 0.f);
   if (st != JL_OK) return st;
   if (B < 0 || total_k < 0 || max_seqlen_k < 0) return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
@@ -151,22 +154,25 @@ int jl_bifocal_prefill_prepare(const void* k, const void* v, int dtype, const in
   c.w_pretrained = w_pretrained;
   c.theta = rope_theta;
   c.ws = workspace;
+  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_prepare(c, s) : jl::launch_prefill_f32_prepare(c, s);
   return hip_status(e, "jl_bifocal_prefill_prepare launch");
 }
 
-int jl_bifocal_prefill_attend(const void* q, const void* k, const void* v, void* o, float* lse,
-                              int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                              int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
-                              int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
-                              double rope_theta, float softmax_scale, const void* workspace,
-                              size_t workspace_bytes, void* stream) {
+int jl_bifocal_prefill_attend_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                                 int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                                 double rope_theta, float softmax_scale, const void* workspace,
+                                 size_t workspace_bytes, void* stream, unsigned flags) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   jl::PrefillCall c;
   const int st = prefill_args(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
                               max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
                               rope_theta, softmax_scale, workspace, workspace_bytes, &c);
   if (st != JL_OK || c.B == 0) return st;
+  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == JL_BF16 ? jl::launch_prefill_bf16_attend(c, s) : jl::launch_prefill_f32_attend(c, s);
   return hip_status(e, "jl_bifocal_prefill_attend launch");
@@ -178,11 +184,12 @@ size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int
   return jl::decode_ws_bytes(B, max_L, Hq, Hkv, head_dim);
 }
 
-int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
-                      int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
-                      const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
-                      int w_pretrained, int w0, double rope_theta, float softmax_scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
+                         int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
+                         const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
+                         int w_pretrained, int w0, double rope_theta, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream, unsigned flags) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
   if (st != JL_OK) return st;
   if (Hq / Hkv > 16) return fail(JL_ERR_UNSUPPORTED, "decode supports up to 16 query heads per KV head (got %d)", Hq / Hkv);
@@ -212,8 +219,49 @@ int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, i
   c.theta = rope_theta;
   c.scale = resolve_scale(softmax_scale, head_dim);
   c.ws = workspace;
+  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
   return hip_status(jl::launch_decode(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
                     "jl_bifocal_decode launch");
+}
+
+int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                       int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta,
+                       float softmax_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return jl_bifocal_prefill_ex(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                               max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta,
+                               softmax_scale, workspace, workspace_bytes, stream, 0u);
+}
+
+int jl_bifocal_prefill_prepare(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,
+                               int B, int total_k, int max_seqlen_k, int Hkv, int head_dim,
+                               int w_pretrained, double rope_theta, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return jl_bifocal_prefill_prepare_ex(k, v, dtype, cu_seqlens_k, B, total_k, max_seqlen_k, Hkv, head_dim,
+                                       w_pretrained, rope_theta, workspace, workspace_bytes, stream, 0u);
+}
+
+int jl_bifocal_prefill_attend(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                              double rope_theta, float softmax_scale, const void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return jl_bifocal_prefill_attend_ex(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                                      max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
+                                      rope_theta, softmax_scale, workspace, workspace_bytes, stream, 0u);
+}
+
+int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
+                      int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
+                      const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
+                      int w_pretrained, int w0, double rope_theta, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return jl_bifocal_decode_ex(q, k_cache, v_cache, stride_b, stride_s, stride_h, o, lse, dtype, seq_L, B, max_L,
+                              Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale, workspace,
+                              workspace_bytes, stream, 0u);
 }
 
 int jl_bifocal_remote_positions(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,

@@ -51,6 +51,7 @@ struct Params {
   int slots;  // partial states per (sequence, head, split)
   int w_pretrained, w0;
   float scale_log2;
+  int prerot;  // q and the key cache arrive rotated at their true positions
 };
 
 template <int D>
@@ -121,7 +122,7 @@ struct SplitState {
 // One 16-key block starting at j0 (wave-uniform).  q0 = j0 / G, r0 = j0 % G.
 // TAIL: the block may run past kend; rows are clamped to kend-1 and their
 // probabilities are zero.
-template <int D, int NR, bool TAIL>
+template <int D, int NR, bool TAIL, bool PR>
 __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&qrf)[D / 32],
                                             SplitState<D>& st, int j0, int q0, int r0) {
   constexpr int NT = D / 32;
@@ -159,15 +160,19 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   // fp32: (n + 1/2) / G lies at least 1/(2G) from an integer and the product
   // with the rounded reciprocal errs by under (G + 16) 2^-23 / G.  Rows past
   // kend (tail only) read table row 0.
+  // PR (pre-rotated cache): local keys are used as stored (row 0: cos 1,
+  // sin 0) and remote keys get R(f(j) - j), i.e. row j - f(j) with sin negated
   const bool klocal = c.qpos - jk < c.w0;
   int kpos;
   if constexpr (TAIL) {
-    kpos = jk < c.kend ? (klocal ? jk : jk / c.G) : 0;
+    const int fj = jk / c.G;
+    kpos = jk < c.kend ? (klocal ? (PR ? 0 : jk) : (PR ? jk - fj : fj)) : 0;
   } else {
     const int frem = c.G < (1 << 20) ? q0 + static_cast<int>((static_cast<float>(r0 + col) + 0.5f) * c.invG)
                                      : jk / c.G;
-    kpos = klocal ? jk : frem;
+    kpos = klocal ? (PR ? 0 : jk) : (PR ? jk - frem : frem);
   }
+  const float ksgn = PR && !klocal ? -1.f : 1.f;
   f16x8 a[NT];
   const float4* cs4 = reinterpret_cast<const float4*>(c.tab + kpos * H + g * 8);
 #pragma unroll
@@ -181,7 +186,7 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
       for (int hh = 0; hh < 2; ++hh) {
         const int e = e2 * 2 + hh;
         const float cc = hh ? cs.z : cs.x;
-        const float sn = hh ? cs.w : cs.y;
+        const float sn = PR ? (hh ? cs.w : cs.y) * ksgn : (hh ? cs.w : cs.y);
         const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
         const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
         a[t][e] = static_cast<_Float16>(x1 * cc - x2 * sn);
@@ -260,7 +265,7 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   }
 }
 
-template <int D, int NR>
+template <int D, int NR, bool PR>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void split_bf16_kernel(Params p) {
   constexpr int NT = D / 32;    // QK^T MFMAs per 16 keys (32 features each)
   constexpr int HT = NT / 2;    // first-half feature groups
@@ -339,7 +344,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
     }
-    const int fq = qpos / G;
+    const RotRow rl = rot_row(qpos, qpos, PR);
+    const RotRow rr = rot_row(qpos / G, qpos, PR);
     const float sc = p.scale_log2;
     f16x8 ql[NT];
 #pragma unroll
@@ -347,8 +353,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = t * 32 + g * 8 + e;
-        const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
-        const float2 cr = p.tab[static_cast<int64_t>(fq) * H + kk];
+        float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+        float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+        cl.y *= rl.sgn;
+        cr.y *= rr.sgn;
         const float x1 = x[t][e], x2 = x[t + HT][e];
         ql[t][e] = static_cast<_Float16>((x1 * cl.x - x2 * cl.y) * sc);
         ql[t + HT][e] = static_cast<_Float16>((x2 * cl.x + x1 * cl.y) * sc);
@@ -385,12 +393,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   int j0 = kbeg + w * kKB;
   int q0 = j0 / G, r0 = j0 % G;
   for (; j0 + kKB <= kend; j0 += step) {
-    split_block<D, NR, false>(c, qrf, st, j0, q0, r0);
+    split_block<D, NR, false, PR>(c, qrf, st, j0, q0, r0);
     q0 += qs;
     r0 += rs;
     if (r0 >= G) { r0 -= G; ++q0; }
   }
-  if (j0 < kend) split_block<D, NR, true>(c, qrf, st, j0, q0, r0);
+  if (j0 < kend) split_block<D, NR, true, PR>(c, qrf, st, j0, q0, r0);
 
   // ---- this wavefront's partial state: O feature nb*16 + col of head
   // g*4 + rr in register rr; m and l of head hh in lane hh
@@ -442,8 +450,12 @@ __global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
     const bool hv = hh < p.ratio;
     const float* src = static_cast<const float*>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * p.ratio + (hv ? hh : 0)) * D;
     const float x1 = hv ? src[kk] : 0.f, x2 = hv ? src[kk + H] : 0.f;
-    const float2 cl = p.tab[static_cast<int64_t>(qpos) * H + kk];
-    const float2 cr = p.tab[static_cast<int64_t>(qpos / G) * H + kk];
+    const RotRow rl = rot_row(qpos, qpos, p.prerot);
+    const RotRow rr = rot_row(qpos / G, qpos, p.prerot);
+    float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+    float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+    cl.y *= rl.sgn;
+    cr.y *= rr.sgn;
     sQ[0][hh][kk] = x1 * cl.x - x2 * cl.y;
     sQ[0][hh][kk + H] = x2 * cl.x + x1 * cl.y;
     sQ[1][hh][kk] = x1 * cr.x - x2 * cr.y;
@@ -464,7 +476,9 @@ __global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
     const int jk = j0 + col;  // this lane's key
     const bool kval = jk < kend;
     const bool klocal = qpos - jk < p.w0;
-    const int kpos = kval ? (klocal ? jk : jk / G) : 0;
+    const RotRow kr_ = rot_row(klocal ? jk : jk / G, jk, p.prerot);
+    const int kpos = kval ? kr_.row : 0;
+    const float ksgn = kr_.sgn;
     float kv[NT][8];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -475,9 +489,10 @@ __global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float2 cs = p.tab[static_cast<int64_t>(kpos) * H + t * 32 + g * 8 + e];
+        const float sn = cs.y * ksgn;
         const float x1 = kv[t][e], x2 = kv[t + HT][e];
-        kv[t][e] = x1 * cs.x - x2 * cs.y;
-        kv[t + HT][e] = x2 * cs.x + x1 * cs.y;
+        kv[t][e] = x1 * cs.x - x2 * sn;
+        kv[t + HT][e] = x2 * cs.x + x1 * sn;
       }
     const float* qsel = klocal ? &sQ[0][0][0] : &sQ[1][0][0];
     float s[NR];
@@ -596,7 +611,10 @@ template <int D, int NR>
 void launch_split(const Params& p, bool bf16, hipStream_t s) {
   if (bf16) {
     const int hw = kWaves / p.wph;
-    hipLaunchKernelGGL((split_bf16_kernel<D, NR>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
+    if (p.prerot)
+      hipLaunchKernelGGL((split_bf16_kernel<D, NR, true>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((split_bf16_kernel<D, NR, false>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
   } else {
     hipLaunchKernelGGL((split_f32_kernel<D, NR>), dim3(p.B * p.Hkv, p.nsplit), dim3(kWavesF32 * 64), 0, s, p);
   }
@@ -672,10 +690,13 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
+  p.prerot = c.prerot ? 1 : 0;
   // rows a decode reads: remote positions (all below w_pretrained) and each
-  // sequence's local window
-  hipError_t e = launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B, c.w0,
-                                        c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s);
+  // sequence's local window; a pre-rotated cache reads row 0 and the
+  // correction rows j - f(j), which cover the whole range
+  hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s)
+                          : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B,
+                                                   c.w0, c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s);
   if (e != hipSuccess) return e;
   const int ratio = c.Hq / c.Hkv;
   if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);

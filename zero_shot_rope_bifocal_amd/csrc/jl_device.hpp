@@ -45,6 +45,22 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// ---------------------------------------------------------------- rotations
+
+// Table row and sign of sin for rotating a vector that sits at position p to
+// angle position a.  Raw inputs: R(a) itself.  Inputs already rotated at p
+// (a pre-rotated cache): the correction R(a - p), with R(-x) read as
+// (cos x, -sin x) from row x ("On-the-Fly Correction Rotation").
+struct RotRow {
+  int row;
+  float sgn;
+};
+__device__ __forceinline__ RotRow rot_row(int a, int p, bool prerot) {
+  if (!prerot) return {a, 1.f};
+  const int d = a - p;
+  return d >= 0 ? RotRow{d, 1.f} : RotRow{-d, -1.f};
+}
+
 // ---------------------------------------------------------------- eq. G / f
 
 // G = max(1, ceil(L / w_pretrained)), exact integers (eq. G).

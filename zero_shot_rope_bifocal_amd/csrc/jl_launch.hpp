@@ -22,6 +22,7 @@ struct PrefillCall {
   double theta;
   float scale;
   void* ws;
+  bool prerot;  // q and k arrive rotated at their true positions
 };
 
 struct DecodeCall {
@@ -37,6 +38,7 @@ struct DecodeCall {
   double theta;
   float scale;
   void* ws;
+  bool prerot;  // q and the key cache arrive rotated at their true positions
 };
 
 // Workspace layouts (bytes).

@@ -55,6 +55,7 @@ struct Params {
   int B, total_q, Hq, Hkv, ratio, ngroups, nqb, max_q, max_k;
   int w_pretrained, w0;
   float scale_log2;   // softmax scale * log2(e)
+  int prerot;         // q and k arrive rotated at their true positions
 };
 
 // First padded key row of sequence b: rows of different sequences never
@@ -96,6 +97,10 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
     const int64_t tok = p.cu_k[b] + pos;
     const int G = group_size(L, p.w_pretrained);
     const int fp = pos / G;
+    // keys at p and at f(p) (or, for a pre-rotated cache, as stored and with
+    // the correction rotation R(f(p) - p))
+    const RotRow rl = rot_row(pos, pos, p.prerot);
+    const RotRow rr = rot_row(fp, pos, p.prerot);
     const uint16_t* src = p.k + (tok * p.Hkv + hk) * D;
     const uint4 a = *reinterpret_cast<const uint4*>(src + c * 8);
     const uint4 bb = *reinterpret_cast<const uint4*>(src + H + c * 8);
@@ -110,8 +115,10 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
         const int kk = c * 8 + e2 * 2 + hh;
         const float x1 = bf16_bits_to_float(static_cast<uint16_t>(xa[e2] >> (16 * hh)));
         const float x2 = bf16_bits_to_float(static_cast<uint16_t>(xb[e2] >> (16 * hh)));
-        const float2 cl = p.tab[static_cast<int64_t>(pos) * H + kk];
-        const float2 cr = p.tab[static_cast<int64_t>(fp) * H + kk];
+        float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+        float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+        cl.y *= rl.sgn;
+        cr.y *= rr.sgn;
         l1[hh] = x1 * cl.x - x2 * cl.y;
         l2[hh] = x2 * cl.x + x1 * cl.y;
         r1[hh] = x1 * cr.x - x2 * cr.y;
@@ -228,19 +235,20 @@ __device__ __forceinline__ void load_query(float (&x)[D / 16][8], const uint16_t
   }
 }
 
-// Rotates this lane's query fragment at position `pos` and scales it by
-// c = softmax_scale * log2(e), so that the MFMA accumulators come out as
-// log2-domain logits.
+// Rotates this lane's query fragment by `rot` (table row and sign of sin, see
+// rot_row) and scales it by c = softmax_scale * log2(e), so that the MFMA
+// accumulators come out as log2-domain logits.
 template <int D>
 __device__ __forceinline__ void rotate_query(f16x8 (&out)[D / 16], const float (&x)[D / 16][8],
-                                             const float2* __restrict__ tab, int pos, int g, float c) {
+                                             const float2* __restrict__ tab, RotRow rot, int g, float c) {
   constexpr int KS = D / 16;
-  const float2* row = tab + static_cast<int64_t>(pos) * (D / 2);
+  const float2* row = tab + static_cast<int64_t>(rot.row) * (D / 2);
 #pragma unroll
   for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 cs = row[ks * 16 + g * 8 + e];
+      float2 cs = row[ks * 16 + g * 8 + e];
+      cs.y *= rot.sgn;
       const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
       out[ks][e] = static_cast<_Float16>((x1 * cs.x - x2 * cs.y) * c);
       out[ks + KS / 2][e] = static_cast<_Float16>((x2 * cs.x + x1 * cs.y) * c);
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid[rb] ? qi[rb] - q_off : 0)) * p.Hq + h) * D;
     float x[KS][8];
     load_query<D>(x, qsrc, qvalid[rb], g);
-    rotate_query<D>(qrf[rb], x, p.tab, pl / G, g, p.scale_log2);
+    rotate_query<D>(qrf[rb], x, p.tab, rot_row(pl / G, pl, p.prerot), g, p.scale_log2);
   }
 
   const uint16_t* kr_base = p.kr + static_cast<int64_t>(hkv) * p.tpad * D;
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid[rb] ? qi[rb] - q_off : 0)) * p.Hq + h) * D;
       float x[KS][8];
       load_query<D>(x, qsrc, qvalid[rb], g);
-      rotate_query<D>(qlf[rb], x, p.tab, pl, g, p.scale_log2);
+      rotate_query<D>(qlf[rb], x, p.tab, rot_row(pl, pl, p.prerot), g, p.scale_log2);
     }
     // window-edge tiles need both logit sets
     int nloc = nrem;
@@ -711,6 +719,7 @@ static Params make_params(const PrefillCall& c) {
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
+  p.prerot = c.prerot ? 1 : 0;
   return p;
 }
 

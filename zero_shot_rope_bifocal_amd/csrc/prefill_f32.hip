@@ -32,6 +32,7 @@ struct Params {
   int B, total_q, Hq, Hkv, ratio, nqb, max_q, max_k;
   int w_pretrained, w0;
   float scale_log2;
+  int prerot;  // q and k arrive rotated at their true positions
 };
 
 template <int D>
@@ -66,13 +67,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Params p) {
   // this lane's query row, rotated at p and f(p)
   {
     const int pl = qvalid ? qi : 0;
-    const int pr = pl / G;
+    const RotRow rl = rot_row(pl, pl, p.prerot);
+    const RotRow rr = rot_row(pl / G, pl, p.prerot);
     const float* src = p.q + (static_cast<int64_t>(qbeg + (qvalid ? qi - q_off : 0)) * p.Hq + h) * D;
     for (int kk = 0; kk < H; ++kk) {
       const float x1 = qvalid ? src[kk] : 0.f;
       const float x2 = qvalid ? src[kk + H] : 0.f;
-      const float2 cl = p.tab[static_cast<int64_t>(pl) * H + kk];
-      const float2 cr = p.tab[static_cast<int64_t>(pr) * H + kk];
+      float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+      float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+      cl.y *= rl.sgn;
+      cr.y *= rr.sgn;
       sQl[t * QSTR + kk] = x1 * cl.x - x2 * cl.y;
       sQl[t * QSTR + kk + H] = x2 * cl.x + x1 * cl.y;
       sQr[t * QSTR + kk] = x1 * cr.x - x2 * cr.y;
@@ -101,8 +105,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Params p) {
         const float* src = p.k + (static_cast<int64_t>(kbeg + j) * p.Hkv + hkv) * D;
         const float x1 = src[kk];
         const float x2 = src[kk + H];
-        const float2 cl = p.tab[static_cast<int64_t>(j) * H + kk];
-        const float2 cr = p.tab[static_cast<int64_t>(j / G) * H + kk];
+        const RotRow rl = rot_row(j, j, p.prerot);
+        const RotRow rr = rot_row(j / G, j, p.prerot);
+        float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+        float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+        cl.y *= rl.sgn;
+        cr.y *= rr.sgn;
         l1 = x1 * cl.x - x2 * cl.y;
         l2 = x2 * cl.x + x1 * cl.y;
         r1 = x1 * cr.x - x2 * cr.y;
@@ -195,6 +203,7 @@ hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s) {
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
+  p.prerot = c.prerot ? 1 : 0;
   const dim3 grid(p.nqb, c.Hq, c.B);
   if (c.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, p);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, p);
