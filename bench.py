@@ -103,6 +103,8 @@ def main():
                     help="run one stage only (for profiling); the JSON line then covers that stage")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-plain", action="store_true",
+                    help="skip the plain-RoPE baseline measured after the timed steps")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -203,6 +205,38 @@ def main():
                             "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
     dtraffic = load_traffic("decode_split", ddigest)
 
+    # plain RoPE causal attention on the same kernels, after the timed region:
+    # prefill with G = 1 and w0 = 0 (every pair at its true position), decode
+    # over a pre-rotated cache with every key in the window (no rotation).
+    plain = None
+    if not args.no_plain:
+        log("plain-RoPE baseline")
+
+        def clock(fn, reps=2):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        plain = {"definition": "prefill: same kernels with w_pretrained = L (G = 1) and w0 = 0; decode: "
+                               "pre-rotated cache, w0 >= L (every key used as stored)"}
+        if do_prefill:
+            jl.prefill_prepare(k, v, cu, L, L, wp_["theta"], Hq=Hq, workspace=ws)
+            p_ms = clock(lambda: jl.prefill_attend(q, k, v, cu, L, L, 0, wp_["theta"], ws, out=o))
+            plain["prefill_attend_ms"] = round(p_ms, 3)
+            plain["prefill_attend_TFLOPs"] = round(fl / (p_ms * 1e-3) / 1e12, 2)
+            plain["bifocal_over_plain_prefill_speed"] = round(p_ms / attn_ms, 4)
+        if do_decode:
+            d_ms = clock(lambda: jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["L"] + 1, wd["theta"], out=do,
+                                           workspace=dws, prerotated=True), reps=5)
+            plain["decode_ms"] = round(d_ms, 4)
+            plain["bifocal_decode_overhead"] = round(dec_ms / d_ms - 1.0, 4)
+
     cpu = None
     if not args.no_cpu_baseline and do_prefill:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
@@ -261,6 +295,7 @@ def main():
             "traffic": dtraffic,
         },
         "cpu_baseline": cpu,
+        "plain_rope_baseline": plain,
     }
     print(json.dumps(line), flush=True)
 
