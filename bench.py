@@ -105,6 +105,8 @@ def main():
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--no-plain", action="store_true",
                     help="skip the plain-RoPE baseline measured after the timed steps")
+    ap.add_argument("--no-ie", action="store_true",
+                    help="skip the inclusion-exclusion route measured after the timed steps")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -237,6 +239,31 @@ def main():
             plain["decode_ms"] = round(d_ms, 4)
             plain["bifocal_decode_overhead"] = round(dec_ms / d_ms - 1.0, 4)
 
+    # the pages' own route to the same prefill (three passes + LSE merge), on
+    # the same inputs, after the timed region
+    ie = None
+    if not args.no_ie and do_prefill:
+        log("inclusion-exclusion route")
+        iws = torch.empty(jl.prefill_ie_workspace_size(jl.JL_BF16, 1, L, L, L, Hq, Hkv, d), dtype=torch.uint8,
+                          device=dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        run_ie = lambda: jl.prefill_ie(q, k, v, cu, L, wp_["w_pretrained"], wp_["w0"], wp_["theta"],  # noqa: E731
+                                       out=o, workspace=iws)
+        run_ie()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(2):
+            run_ie()
+        b.record()
+        torch.cuda.synchronize()
+        ie_ms = a.elapsed_time(b) / 2
+        ie = {"definition": "prepare + window pass (true positions) + full causal pass (grouped positions) + "
+                            "window pass (grouped positions) + LSE merge, fp32 pass outputs",
+              "prefill_ms": round(ie_ms, 3),
+              "TFLOPs_equiv": round(fl / (ie_ms * 1e-3) / 1e12, 2),
+              "routed_over_ie_speed": round(ie_ms / (prep_ms + attn_ms), 4)}
+        del iws
+
     cpu = None
     if not args.no_cpu_baseline and do_prefill:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
@@ -296,6 +323,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "plain_rope_baseline": plain,
+        "inclusion_exclusion_route": ie,
     }
     print(json.dumps(line), flush=True)
 

@@ -160,6 +160,30 @@ int jl_bifocal_prefill_attend_ex(const void* q, const void* k, const void* v, vo
                                  double rope_theta, float softmax_scale, const void* workspace,
                                  size_t workspace_bytes, void* stream, unsigned flags);
 
+/* The same prefill result by the pages' own route, the inclusion-exclusion
+ * attention merge ("Inference Efficiency Mechanisms"): three attention passes
+ * with fp32 output and LSE, (1) the pairs closer than w0 rotated at their
+ * true positions, (2) every causal pair rotated at the grouped positions
+ * f(p), (3) the pairs closer than w0 at f(p), then per row
+ *   O = (w1 O1 + w2 O2 - w3 O3) / (w1 + w2 - w3), w_i = exp(LSE_i - M),
+ *   M = max(LSE_1, LSE_2), LSE = M + log(w1 + w2 - w3).
+ * Arguments, flags and error behaviour as jl_bifocal_prefill_ex; the
+ * workspace (256-byte aligned, caller-owned, scratch between calls) must
+ * hold jl_bifocal_prefill_ie_workspace_size(...) bytes: the prefill
+ * workspace plus three fp32 [total_q, Hq, head_dim] rows and three fp32
+ * [Hq, total_q] LSE buffers.  It exists to compare against the tile-routed
+ * jl_bifocal_prefill: it does about the work of a full causal pass plus two
+ * window passes, and the difference w2 - w3 cancels when a row's grouped-
+ * position mass sits inside the window. */
+size_t jl_bifocal_prefill_ie_workspace_size(int dtype, int B, int total_q, int total_k,
+                                            int max_seqlen_k, int Hq, int Hkv, int head_dim);
+int jl_bifocal_prefill_ie(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                          int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                          double rope_theta, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream, unsigned flags);
+
 /* Bytes of device workspace jl_bifocal_decode needs, or 0 on invalid sizes. */
 size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv,
                                         int head_dim);

@@ -124,3 +124,26 @@ def test_unknown_flags_rejected():
     assert rc == -1 and b"flag" in L.jl_last_error()
     rc = L.jl_bifocal_prefill_prepare_ex(None, None, 1, None, 1, 1, 1, 1, 128, 1, 1e4, None, 0, None, 8)
     assert rc == -1 and b"flag" in L.jl_last_error()
+
+
+def test_prefill_ie_workspace_and_rejections():
+    """The merged route needs the prefill workspace plus three fp32 O rows and
+    three LSE rows; it rejects an undersized workspace, bad sizes and unknown
+    flags before any HIP call."""
+    L = _lib()
+    base = jl.prefill_workspace_size(jl.JL_BF16, 1, 4096, 4096, 32, 8, 128)
+    ie = jl.prefill_ie_workspace_size(jl.JL_BF16, 1, 4096, 4096, 4096, 32, 8, 128)
+    assert ie >= base + 3 * 4096 * 32 * 128 * 4 + 3 * 32 * 4096 * 4
+    assert jl.prefill_ie_workspace_size(jl.JL_F32, 1, 100, 100, 100, 2, 2, 64) >= 3 * 100 * 2 * 64 * 4
+    assert jl.prefill_ie_workspace_size(5, 1, 1, 1, 1, 1, 1, 64) == 0
+    vp = ctypes.c_void_p
+    small = jl.prefill_workspace_size(jl.JL_BF16, 1, 64, 64, 8, 2, 128)
+    assert small < jl.prefill_ie_workspace_size(jl.JL_BF16, 1, 64, 64, 64, 8, 2, 128)
+    args = [vp(1), vp(1), vp(1), vp(1), None, jl.JL_BF16, vp(1), None, 1, 64, 64, 64, 64, 8, 2, 128, 32, 4, 1e4,
+            0.0, vp(256), small, None]
+    assert L.jl_bifocal_prefill_ie(*args, 0) == -3          # the plain prefill workspace is too small
+    assert b"needed" in L.jl_last_error()
+    bad = list(args)
+    bad[15] = 96
+    assert L.jl_bifocal_prefill_ie(*bad, 0) == -2
+    assert L.jl_bifocal_prefill_ie(*args, 4) == -1 and b"flag" in L.jl_last_error()

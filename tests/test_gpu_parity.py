@@ -271,3 +271,27 @@ def test_decode_equals_last_prefill_row():
     seq = torch.tensor([L], dtype=torch.int32).cuda()
     o_d = jl.decode(q, k, v, seq, 256, 100, 1e4).cpu().numpy()
     assert np.max(np.abs(o_d[0] - o_p[L - 1])) < 1e-5
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_steps_across_G_boundaries(dt):
+    """Decode steps on one unchanged cache as the length crosses multiples of
+    w_pretrained: G goes 1, 1, 2, 2, 3, 3, 4 without any key being rewritten."""
+    torch = _torch()
+    wp, w0, theta, S = 256, 64, 1e4, 1024
+    seq_L = [wp - 1, wp, wp + 1, 2 * wp, 2 * wp + 1, 3 * wp, 3 * wp + 1]
+    _say("decode across G boundaries", dt, seq_L)
+    one = W.decode_inputs(1, S, 8, 2, 128, dt, 38)
+    B = len(seq_L)
+    inp = dict(q=np.repeat(one["q"], B, axis=0), k=np.repeat(one["k"], B, axis=0),
+               v=np.repeat(one["v"], B, axis=0), seq_L=np.asarray(seq_L, dtype=np.int32), dtype=dt)
+    check_decode(inp, wp, w0, theta)
+    # One cache buffer shared by every step (batch stride 0 view).
+    k = W.to_device(one["k"], dt).expand(B, -1, -1, -1)
+    v = W.to_device(one["v"], dt).expand(B, -1, -1, -1)
+    q = W.to_device(one["q"], dt).expand(B, -1, -1).contiguous()
+    seq = torch.from_numpy(inp["seq_L"]).cuda()
+    out = jl.decode(q, k, v, seq, wp, w0, theta)
+    o_sep, _ = run_decode(inp, wp, w0, theta)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), o_sep)

@@ -93,6 +93,7 @@ DECODE_CASES = [
     (4, 3000, [3000, 1, 2049, 777], 32, 8, 128, "bf16", 512, 256, 1e6, 71),
     (2, 1000, [1000, 333], 8, 2, 64, "bf16", 200, 0, 1e4, 72),
     (3, 800, [800, 65, 5], 8, 2, 128, "f32", 100, 50, 1e4, 73),
+    (7, 1024, [255, 256, 257, 512, 513, 768, 769], 8, 2, 128, "bf16", 256, 64, 1e4, 75),  # G 1..4
 ]
 
 

@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "JL_F32", "JL_BF16", "JL_FLAG_PREROTATED", "JetLongError", "library_path", "lib",
-    "group_size", "prefill", "prefill_prepare", "prefill_attend", "decode", "prefill_workspace_size", "decode_workspace_size",
+    "group_size", "prefill", "prefill_prepare", "prefill_attend", "prefill_ie", "decode", "prefill_workspace_size",
+    "prefill_ie_workspace_size", "decode_workspace_size",
     "remote_positions", "tile_classes", "prefill_tile_shape", "version",
 ]
 
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.jl_bifocal_prefill_attend_ex.restype = c_int
     L.jl_bifocal_decode_ex.argtypes = L.jl_bifocal_decode.argtypes + [c_u]
     L.jl_bifocal_decode_ex.restype = c_int
+    L.jl_bifocal_prefill_ie_workspace_size.argtypes = [c_int] * 8
+    L.jl_bifocal_prefill_ie_workspace_size.restype = c_sz
+    L.jl_bifocal_prefill_ie.argtypes = L.jl_bifocal_prefill_ex.argtypes
+    L.jl_bifocal_prefill_ie.restype = c_int
     L.jl_bifocal_remote_positions.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     L.jl_bifocal_remote_positions.restype = c_int
     L.jl_bifocal_tile_classes.argtypes = [c_int] * 5 + [c_vp, c_vp]
@@ -141,6 +146,12 @@ def prefill_workspace_size(dtype: int, B: int, total_k: int, max_seqlen_k: int, 
     return int(lib().jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hq, Hkv, head_dim))
 
 
+def prefill_ie_workspace_size(dtype: int, B: int, total_q: int, total_k: int, max_seqlen_k: int, Hq: int,
+                              Hkv: int, head_dim: int) -> int:
+    return int(lib().jl_bifocal_prefill_ie_workspace_size(dtype, B, total_q, total_k, max_seqlen_k, Hq, Hkv,
+                                                          head_dim))
+
+
 def decode_workspace_size(dtype: int, B: int, max_L: int, Hq: int, Hkv: int, head_dim: int) -> int:
     return int(lib().jl_bifocal_decode_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim))
 
@@ -153,6 +164,21 @@ def prefill(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int
     sequence b sit at its last Lq_b positions.  prerotated: q and k hold
     R(p) q, R(p) k (a RoPE cache).  Returns out (and lse [Hq, Tq] float32 when
     asked)."""
+    return _prefill(False, q, k, v, cu_seqlens_q, max_seqlen_q, w_pretrained, w0, rope_theta, cu_seqlens_k,
+                    max_seqlen_k, softmax_scale, out, lse, workspace, return_lse, prerotated)
+
+
+def prefill_ie(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int, rope_theta: float,
+               cu_seqlens_k=None, max_seqlen_k: int | None = None, softmax_scale: float = 0.0,
+               out=None, lse=None, workspace=None, return_lse: bool = False, prerotated: bool = False):
+    """``prefill`` computed by the inclusion-exclusion merge of three attention
+    passes (a comparison route; same arguments and result)."""
+    return _prefill(True, q, k, v, cu_seqlens_q, max_seqlen_q, w_pretrained, w0, rope_theta, cu_seqlens_k,
+                    max_seqlen_k, softmax_scale, out, lse, workspace, return_lse, prerotated)
+
+
+def _prefill(ie, q, k, v, cu_seqlens_q, max_seqlen_q, w_pretrained, w0, rope_theta, cu_seqlens_k, max_seqlen_k,
+             softmax_scale, out, lse, workspace, return_lse, prerotated):
     torch = _torch()
     _need_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
     for t in (q, k, v):
@@ -174,10 +200,12 @@ def prefill(q, k, v, cu_seqlens_q, max_seqlen_q: int, w_pretrained: int, w0: int
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
-    need = prefill_workspace_size(dt, B, Tk, max_seqlen_k, Hq, Hkv, d)
+    need = (prefill_ie_workspace_size(dt, B, Tq, Tk, max_seqlen_k, Hq, Hkv, d) if ie
+            else prefill_workspace_size(dt, B, Tk, max_seqlen_k, Hq, Hkv, d))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    code = lib().jl_bifocal_prefill_ex(
+    entry = lib().jl_bifocal_prefill_ie if ie else lib().jl_bifocal_prefill_ex
+    code = entry(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), dt, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, int(w_pretrained), int(w0),
         float(rope_theta), float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(q.device),

@@ -68,6 +68,14 @@ size_t jl_bifocal_prefill_workspace_size(int dtype, int B, int total_k, int max_
   return jl::prefill_ws_bytes_f32(max_seqlen_k, head_dim);
 }
 
+size_t jl_bifocal_prefill_ie_workspace_size(int dtype, int B, int total_q, int total_k, int max_seqlen_k, int Hq,
+                                            int Hkv, int head_dim) {
+  if (!supported_dtype(dtype) || !supported_dim(head_dim) || B < 0 || total_q < 0 || total_k < 0 ||
+      max_seqlen_k < 0 || Hq < 1 || Hkv < 1)
+    return 0;
+  return jl::prefill_ie_ws_bytes(dtype == JL_BF16, B, total_q, total_k, max_seqlen_k, Hq, Hkv, head_dim);
+}
+
 }  // extern "C"
 
 namespace {
@@ -78,7 +86,7 @@ int prefill_args(const void* q, const void* k, const void* v, void* o, float* ls
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
                  int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int head_dim,
                  int w_pretrained, int w0, double rope_theta, float softmax_scale, const void* workspace,
-                 size_t workspace_bytes, jl::PrefillCall* c) {
+                 size_t workspace_bytes, jl::PrefillCall* c, bool ie = false) {
   *c = jl::PrefillCall{};
   int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
   if (st != JL_OK) return st;
@@ -91,7 +99,8 @@ int prefill_args(const void* q, const void* k, const void* v, void* o, float* ls
   if (!cu_seqlens_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_q must be non-null");
   if (!cu_seqlens_k && total_k != total_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_k is NULL but total_k != total_q");
   if (max_seqlen_k < 1) return fail(JL_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 for a non-empty batch");
-  const size_t need = jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hq, Hkv, head_dim);
+  const size_t need = ie ? jl_bifocal_prefill_ie_workspace_size(dtype, B, total_q, total_k, max_seqlen_k, Hq, Hkv, head_dim)
+                        : jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hq, Hkv, head_dim);
   if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -130,6 +139,22 @@ int jl_bifocal_prefill_ex(const void* q, const void* k, const void* v, void* o, 
   if (e != hipSuccess) return hip_status(e, "jl_bifocal_prefill prepare launch");
   e = dtype == JL_BF16 ? jl::launch_prefill_bf16_attend(c, s) : jl::launch_prefill_f32_attend(c, s);
   return hip_status(e, "jl_bifocal_prefill attend launch");
+}
+
+int jl_bifocal_prefill_ie(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
+                          int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int head_dim,
+                          int w_pretrained, int w0, double rope_theta, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* stream, unsigned flags) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  jl::PrefillCall c;
+  const int st = prefill_args(q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                              max_seqlen_q, max_seqlen_k, Hq, Hkv, head_dim, w_pretrained, w0,
+                              rope_theta, softmax_scale, workspace, workspace_bytes, &c, true);
+  if (st != JL_OK || c.B == 0) return st;
+  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
+  return hip_status(jl::launch_prefill_ie(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_prefill_ie launch");
 }
 
 int jl_bifocal_prefill_prepare_ex(const void* k, const void* v, int dtype, const int32_t* cu_seqlens_k,

@@ -62,6 +62,17 @@ hipError_t launch_prefill_bf16_attend(const PrefillCall& c, hipStream_t s);
 hipError_t launch_prefill_f32_prepare(const PrefillCall& c, hipStream_t s);
 hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s);
 hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s);
+
+// Inclusion-exclusion route to the same prefill result: three attention
+// passes with fp32 output rows [total_q][Hq][D] and LSE [Hq][total_q], then a
+// merge.  The passes read the workspace of a finished prepare.
+enum IePass : int { kIeWindowLocal = 1, kIeFullRemote = 2, kIeWindowRemote = 3 };
+hipError_t launch_prefill_bf16_ie_pass(const PrefillCall& c, int pass, float* o, float* lse, hipStream_t s);
+hipError_t launch_prefill_f32_ie_pass(const PrefillCall& c, int pass, float* o, float* lse, hipStream_t s);
+// Workspace of the merged route: the prefill workspace, then three fp32 O
+// and three LSE buffers.
+size_t prefill_ie_ws_bytes(bool bf16, int B, int total_q, int total_k, int max_k, int Hq, int Hkv, int D);
+hipError_t launch_prefill_ie(const PrefillCall& c, bool bf16, hipStream_t s);
 hipError_t launch_remote_positions(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q,
                                    int w_pretrained, int32_t* pos, int32_t* f, int32_t* G,
                                    hipStream_t s);

@@ -56,7 +56,18 @@ struct Params {
   int w_pretrained, w0;
   float scale_log2;   // softmax scale * log2(e)
   int prerot;         // q and k arrive rotated at their true positions
+  float* o32;         // fp32 output rows of a merge pass (MODE != kModeBifocal)
+  int band_remote;    // window pass at the grouped positions (kModeWindow)
 };
+
+// What one attention launch computes.  kModeBifocal is the routed result.
+// The other two are passes of the inclusion-exclusion merge, with fp32
+// output: kModeFull is plain causal attention over every key with one
+// rotation (the caller passes w0 = 0, so every pair takes the grouped
+// positions); kModeWindow keeps only the pairs closer than w0, rotated at
+// the true positions, or at the grouped ones when band_remote is set (the
+// caller then points kl at the grouped key copy).
+enum : int { kModeBifocal = 0, kModeFull = 1, kModeWindow = 2 };
 
 // First padded key row of sequence b: rows of different sequences never
 // share a 64-row tile, and every sequence owns its tail rows up to the next
@@ -387,8 +398,9 @@ __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
 // when it straddles the window edge); MASK adds the causal and
 // end-of-sequence mask.  Lane (r32, g) holds query qi[rb]; accumulator
 // register r of key block kb holds key j0g + kb*32 + (r/4)*8 + r%4 (j0g =
-// tile start + g*4).
-template <int D, int NRB, bool USE_R, bool USE_L, bool MASK>
+// tile start + g*4).  BAND drops the pairs at distance >= w0 (window passes
+// of the merge) and lets a row stay empty (running max -inf) over a tile.
+template <int D, int NRB, bool USE_R, bool USE_L, bool MASK, bool BAND = false>
 __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ kl_lane,
                                           const uint16_t* __restrict__ v_lane,
@@ -416,12 +428,15 @@ __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
         else if constexpr (USE_R) s = sr[rb][kb][r];
         else s = sl[rb][kb][r];
         if constexpr (MASK) s = (kj > qi[rb] || kj >= L) ? -INFINITY : s;
+        if constexpr (BAND) s = (qi[rb] - kj >= w0) ? -INFINITY : s;
         t[kb][r] = s;
         mx = fmaxf(mx, s);
       }
     mx = xhalf_max(mx);
     const float m_new = fmaxf(m_run[rb], mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+    float m_use = m_new;
+    if constexpr (BAND) m_use = m_new == -INFINITY ? 0.f : m_new;  // empty so far: p = 0, no NaN
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
     l_run[rb] *= alpha;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -431,14 +446,15 @@ __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[kb][r] -= m_new;
+      for (int r = 0; r < 16; ++r) t[kb][r] -= m_use;
     l_run[rb] += probs(t, pf[rb]);
   }
   pv<D, NRB>(v_lane, pf, acc);
 }
 
-template <int D, int HPW, int NRB>
+template <int D, int HPW, int NRB, int MODE>
 __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
+  constexpr bool BAND = MODE == kModeWindow;
   constexpr int NW = 8 / NRB;       // wavefronts per workgroup
   constexpr int NT = NW * 64;       // threads per workgroup
   constexpr int ROWS = 32 * 8 / HPW;  // query positions per workgroup
@@ -526,10 +542,22 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
   while (nrem < nkt && (classify_tile(i0, i1, nrem * kBN, min(L, nrem * kBN + kBN) - 1, p.w0) & 3) == kRemote) ++nrem;
   auto cls_of = [&](int kt) { return classify_tile(i0, i1, kt * kBN, min(L, kt * kBN + kBN) - 1, p.w0); };
 
+  // a window pass starts at the first tile that holds a pair inside w0
+  const int kt0 = BAND ? nrem : 0;
   TileRegs<D * kBN / 8 / NT> tr;
-  int cls = cls_of(0);
-  load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
-  store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tid);
+  int cls;
+  if constexpr (BAND) {
+    cls = 0;
+    if (kt0 < nkt) {
+      cls = cls_of(kt0);
+      load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt0) * kBN, cls, tid);
+      store_tile<D, NT>(tr, sKr[kt0 & 1], sKl[kt0 & 1], sV[kt0 & 1], cls, tid);
+    }
+  } else {
+    cls = cls_of(0);
+    load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
+    store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tid);
+  }
   __syncthreads();
 
   // ---- all-remote tiles: remote query only.  The inner loop is the fast
@@ -537,9 +565,9 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
   // tile) is redone by the slow path, which then re-enters the fast loop.
   // The next tile's global loads are issued at the top of every iteration,
   // before the current tile is computed, and stored to LDS after it.
-  int kt = 0;
+  int kt = kt0;
   int ncls = 0;
-  while (kt < nrem) {
+  while (!BAND && kt < nrem) {
     for (; kt < nrem; ++kt) {
       const int buf = kt & 1;
       ncls = 0;
@@ -577,7 +605,8 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       const uint16_t* qsrc = p.q + (static_cast<int64_t>(qbeg + (qvalid[rb] ? qi[rb] - q_off : 0)) * p.Hq + h) * D;
       float x[KS][8];
       load_query<D>(x, qsrc, qvalid[rb], g);
-      rotate_query<D>(qlf[rb], x, p.tab, rot_row(pl, pl, p.prerot), g, p.scale_log2);
+      const int pa = BAND && p.band_remote ? pl / G : pl;
+      rotate_query<D>(qlf[rb], x, p.tab, rot_row(pa, pl, p.prerot), g, p.scale_log2);
     }
     // window-edge tiles need both logit sets
     int nloc = nrem;
@@ -593,10 +622,17 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       const uint16_t* krl = sKr[buf] + kr_off;
       const uint16_t* kll = sKl[buf] + kr_off;
       const uint16_t* vl = sV[buf] + v_off;
-      if ((cls & kDiag) || kt * kBN + kBN > L)
-        tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-      else
-        tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+      if constexpr (BAND) {
+        if ((cls & kDiag) || kt * kBN + kBN > L)
+          tile_slow<D, NRB, false, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else
+          tile_slow<D, NRB, false, true, false, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+      } else {
+        if ((cls & kDiag) || kt * kBN + kBN > L)
+          tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+        else
+          tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+      }
       if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
       __syncthreads();
       cls = ncls;
@@ -622,11 +658,11 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         const int buf = kt & 1;
         const int j0g = kt * kBN + g * 4;
         if ((cls & kDiag) || kt * kBN + kBN > L)
-          tile_slow<D, NRB, false, true, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
-                                               acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, true, BAND>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf,
+                                                     qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
         else
-          tile_slow<D, NRB, false, true, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
-                                                acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, false, BAND>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf,
+                                                      qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
         if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
         __syncthreads();
         cls = ncls;
@@ -636,6 +672,28 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
   }
 
   // ---- epilogue: lane holds query qi[rb], features mb*32 + (r/4)*8 + g*4 + r%4
+  if constexpr (MODE != kModeBifocal) {
+    // merge pass: fp32 rows; a window pass with w0 = 0 holds no pair at all
+    // (O = 0, LSE = -inf)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (!qvalid[rb]) continue;
+      const bool empty = !(l_run[rb] > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_run[rb];
+      const int64_t tok = qbeg + qi[rb] - q_off;
+      float* dst = p.o32 + (tok * p.Hq + h) * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + mb * 32 + q4 * 8 + g * 4) =
+              make_float4(acc[rb][mb][q4 * 4 + 0] * inv, acc[rb][mb][q4 * 4 + 1] * inv,
+                          acc[rb][mb][q4 * 4 + 2] * inv, acc[rb][mb][q4 * 4 + 3] * inv);
+      if (g == 0)
+        p.lse[static_cast<int64_t>(h) * p.total_q + tok] = empty ? -INFINITY : (m_run[rb] + log2f(l_run[rb])) * kLn2;
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (!qvalid[rb]) continue;
@@ -661,13 +719,27 @@ int heads_per_wg(int ratio) { return ratio % 4 == 0 ? 4 : (ratio % 2 == 0 ? 2 : 
 // 2: 4 waves of 64 rows).
 constexpr int kNRB = JL_PREFILL_NRB;
 
-template <int D, int HPW>
+template <int D, int HPW, int MODE>
 hipError_t launch_attn(const Params& prm, int nqb, hipStream_t s) {
   const int units = prm.B * prm.Hkv * prm.ngroups;
   const int64_t blocks = static_cast<int64_t>(nqb) * units;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, HPW, kNRB>), dim3(static_cast<unsigned>(blocks)), dim3(64 * 8 / kNRB), 0, s, prm);
+  hipLaunchKernelGGL((attn_kernel<D, HPW, kNRB, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * 8 / kNRB), 0,
+                     s, prm);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_attn_mode(const Params& p, int D, hipStream_t s) {
+  const int hpw = heads_per_wg(p.ratio);
+  if (D == 128) {
+    if (hpw == 4) return launch_attn<128, 4, MODE>(p, p.nqb, s);
+    if (hpw == 2) return launch_attn<128, 2, MODE>(p, p.nqb, s);
+    return launch_attn<128, 1, MODE>(p, p.nqb, s);
+  }
+  if (hpw == 4) return launch_attn<64, 4, MODE>(p, p.nqb, s);
+  if (hpw == 2) return launch_attn<64, 2, MODE>(p, p.nqb, s);
+  return launch_attn<64, 1, MODE>(p, p.nqb, s);
 }
 
 }  // namespace
@@ -736,16 +808,23 @@ hipError_t launch_prefill_bf16_prepare(const PrefillCall& c, hipStream_t s) {
 
 hipError_t launch_prefill_bf16_attend(const PrefillCall& c, hipStream_t s) {
   if (c.total_q == 0 || c.B == 0) return hipSuccess;
-  const Params p = make_params(c);
-  const int hpw = heads_per_wg(p.ratio);
-  if (c.D == 128) {
-    if (hpw == 4) return launch_attn<128, 4>(p, p.nqb, s);
-    if (hpw == 2) return launch_attn<128, 2>(p, p.nqb, s);
-    return launch_attn<128, 1>(p, p.nqb, s);
+  return launch_attn_mode<kModeBifocal>(make_params(c), c.D, s);
+}
+
+hipError_t launch_prefill_bf16_ie_pass(const PrefillCall& c, int pass, float* o, float* lse, hipStream_t s) {
+  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+  Params p = make_params(c);
+  p.o32 = o;
+  p.lse = lse;
+  if (pass == kIeFullRemote) {
+    p.w0 = 0;
+    return launch_attn_mode<kModeFull>(p, c.D, s);
   }
-  if (hpw == 4) return launch_attn<64, 4>(p, p.nqb, s);
-  if (hpw == 2) return launch_attn<64, 2>(p, p.nqb, s);
-  return launch_attn<64, 1>(p, p.nqb, s);
+  if (pass == kIeWindowRemote) {
+    p.band_remote = 1;
+    p.kl = p.kr;
+  }
+  return launch_attn_mode<kModeWindow>(p, c.D, s);
 }
 
 }  // namespace jl

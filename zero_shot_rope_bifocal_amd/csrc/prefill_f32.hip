@@ -33,6 +33,10 @@ struct Params {
   int w_pretrained, w0;
   float scale_log2;
   int prerot;  // q and k arrive rotated at their true positions
+  // 0: the routed result.  Window passes of the inclusion-exclusion merge,
+  // only pairs closer than w0: 1 rotated at the true positions, 2 at the
+  // grouped ones.  (Its full pass is mode 0 with w0 = 0.)
+  int mode;
 };
 
 template <int D>
@@ -92,7 +96,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Params p) {
   const float* qrrow = &sQr[t * QSTR];
 
   const int nkt = i1 / kBN + 1;
-  for (int kt = 0; kt < nkt; ++kt) {
+  const int kt0 = p.mode ? max(0, i0 - p.w0 + 1) / kBN : 0;
+  for (int kt = kt0; kt < nkt; ++kt) {
     const int j0 = kt * kBN;
     __syncthreads();
     // rotate the raw key tile at both angle sets into LDS
@@ -134,8 +139,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Params p) {
     for (int jj = 0; jj < kBN; ++jj) {
       const int j = j0 + jj;
       float sc = -INFINITY;
-      if (j <= qi && j < L) {
-        const bool local = qi - j < p.w0;
+      const bool in_window = qi - j < p.w0;
+      if (j <= qi && j < L && (p.mode == 0 || in_window)) {
+        const bool local = p.mode == 0 ? in_window : p.mode == 1;
         const float* qv = local ? qlrow : qrrow;
         const float* kv = local ? &sKl[jj * D] : &sKr[jj * D];
         float dot = 0.f;
@@ -163,10 +169,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Params p) {
   if (qvalid) {
     const int64_t tok = qbeg + qi - q_off;
     float* dst = p.o + (tok * p.Hq + h) * D;
-    const float inv = 1.f / l_run;
+    // only a window pass with w0 = 0 sees no key at all: O = 0, LSE = -inf
+    const bool empty = !(l_run > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_run;
 #pragma unroll
     for (int e = 0; e < D; ++e) dst[e] = acc[e] * inv;
-    if (p.lse) p.lse[static_cast<int64_t>(h) * p.total_q + tok] = (m_run + log2f(l_run)) * kLn2;
+    if (p.lse) p.lse[static_cast<int64_t>(h) * p.total_q + tok] = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
   }
 }
 
@@ -181,8 +189,7 @@ hipError_t launch_prefill_f32_prepare(const PrefillCall& c, hipStream_t s) {
   return launch_rope_table(static_cast<float2*>(c.ws), c.max_k, c.D, c.theta, s);
 }
 
-hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s) {
-  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+static Params make_params(const PrefillCall& c) {
   Params p{};
   p.q = static_cast<const float*>(c.q);
   p.k = static_cast<const float*>(c.k);
@@ -204,10 +211,29 @@ hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s) {
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
   p.prerot = c.prerot ? 1 : 0;
-  const dim3 grid(p.nqb, c.Hq, c.B);
-  if (c.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, p);
+  return p;
+}
+
+static hipError_t launch(const Params& p, int D, hipStream_t s) {
+  const dim3 grid(p.nqb, p.Hq, p.B);
+  if (D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, p);
   else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32_attend(const PrefillCall& c, hipStream_t s) {
+  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+  return launch(make_params(c), c.D, s);
+}
+
+hipError_t launch_prefill_f32_ie_pass(const PrefillCall& c, int pass, float* o, float* lse, hipStream_t s) {
+  if (c.total_q == 0 || c.B == 0) return hipSuccess;
+  Params p = make_params(c);
+  p.o = o;
+  p.lse = lse;
+  if (pass == kIeFullRemote) p.w0 = 0;
+  else p.mode = pass == kIeWindowLocal ? 1 : 2;
+  return launch(p, c.D, s);
 }
 
 }  // namespace jl
