@@ -319,6 +319,16 @@ __device__ __forceinline__ void pv(const uint16_t* __restrict__ v_lane, const f1
     for (int rb = 0; rb < NRB; ++rb)
       acc[rb][f % MB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, pf[rb][f / MB], acc[rb][f % MB], 0, 0, 0);
   }
+  // keep the read-ahead the loop above describes: PF reads, then one read per
+  // MFMA, then the last MFMAs (the scheduler otherwise trades it for
+  // registers and waits on every read)
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int f = 0; f < NF - PF; ++f) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
 }
 
 // S^T of a 64-key tile for NRB row blocks (two 32-key blocks each); the
@@ -350,6 +360,16 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
     for (int rb = 0; rb < NRB; ++rb)
       sc[rb][f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, qf[rb][f >> 1], sc[rb][f & 1], 0, 0, 0);
   }
+  // keep the read-ahead the loop above describes: PF reads, then one read per
+  // MFMA, then the last MFMAs (the scheduler otherwise trades it for
+  // registers and waits on every read)
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int f = 0; f < NF - PF; ++f) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NRB * PF, 0);
 }
 
 // Fast path of an unmasked tile scored with one rotation (all-remote, or
@@ -398,9 +418,11 @@ __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
 // when it straddles the window edge); MASK adds the causal and
 // end-of-sequence mask.  Lane (r32, g) holds query qi[rb]; accumulator
 // register r of key block kb holds key j0g + kb*32 + (r/4)*8 + r%4 (j0g =
-// tile start + g*4).  BAND drops the pairs at distance >= w0 (window passes
-// of the merge) and lets a row stay empty (running max -inf) over a tile.
-template <int D, int NRB, bool USE_R, bool USE_L, bool MASK, bool BAND = false>
+// tile start + g*4).  PAIRS keeps only some pairs: kPairsAll, kPairsRemote
+// (distance >= w0) or kPairsWindow (distance < w0); with a selection a row may
+// stay empty over a tile (running max -inf), which is guarded.
+enum : int { kPairsAll = 0, kPairsRemote = 1, kPairsWindow = 2 };
+template <int D, int NRB, bool USE_R, bool USE_L, bool MASK, int PAIRS = kPairsAll>
 __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ kl_lane,
                                           const uint16_t* __restrict__ v_lane,
@@ -428,14 +450,15 @@ __device__ __forceinline__ void tile_slow(const uint16_t* __restrict__ kr_lane,
         else if constexpr (USE_R) s = sr[rb][kb][r];
         else s = sl[rb][kb][r];
         if constexpr (MASK) s = (kj > qi[rb] || kj >= L) ? -INFINITY : s;
-        if constexpr (BAND) s = (qi[rb] - kj >= w0) ? -INFINITY : s;
+        if constexpr (PAIRS == kPairsWindow) s = (qi[rb] - kj >= w0) ? -INFINITY : s;
+        if constexpr (PAIRS == kPairsRemote) s = (qi[rb] - kj < w0) ? -INFINITY : s;
         t[kb][r] = s;
         mx = fmaxf(mx, s);
       }
     mx = xhalf_max(mx);
     const float m_new = fmaxf(m_run[rb], mx);
     float m_use = m_new;
-    if constexpr (BAND) m_use = m_new == -INFINITY ? 0.f : m_new;  // empty so far: p = 0, no NaN
+    if constexpr (PAIRS != kPairsAll) m_use = m_new == -INFINITY ? 0.f : m_new;  // empty so far: p = 0, no NaN
     const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
     l_run[rb] *= alpha;
 #pragma unroll
@@ -624,9 +647,11 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       const uint16_t* vl = sV[buf] + v_off;
       if constexpr (BAND) {
         if ((cls & kDiag) || kt * kBN + kBN > L)
-          tile_slow<D, NRB, false, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, true, kPairsWindow>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L,
+                                                             p.w0);
         else
-          tile_slow<D, NRB, false, true, false, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, false, kPairsWindow>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L,
+                                                              p.w0);
       } else {
         if ((cls & kDiag) || kt * kBN + kBN > L)
           tile_slow<D, NRB, true, true, true>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
@@ -658,11 +683,11 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         const int buf = kt & 1;
         const int j0g = kt * kBN + g * 4;
         if ((cls & kDiag) || kt * kBN + kBN > L)
-          tile_slow<D, NRB, false, true, true, BAND>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf,
-                                                     qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, true, BAND ? kPairsWindow : kPairsAll>(
+              sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
         else
-          tile_slow<D, NRB, false, true, false, BAND>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf,
-                                                      qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
+          tile_slow<D, NRB, false, true, false, BAND ? kPairsWindow : kPairsAll>(
+              sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
         if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
         __syncthreads();
         cls = ncls;
