@@ -193,6 +193,7 @@ def main():
     dec = [e[2].elapsed_time(e[3]) for e in evs]
     tot = [e[0].elapsed_time(e[3]) for e in evs]
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    median = lambda xs: sorted(xs)[len(xs) // 2] if len(xs) % 2 else sum(sorted(xs)[len(xs) // 2 - 1:len(xs) // 2 + 1]) / 2  # noqa: E731
     prep_ms, attn_ms, dec_ms, step_ms = mean(prep), mean(attn), mean(dec), mean(tot)
     fl = prefill_flops(wp_["lens"], Hq, d)
     pre_tflops = fl / ((prep_ms + attn_ms) * 1e-3) / 1e12 if do_prefill else 0.0
@@ -264,6 +265,18 @@ def main():
               "routed_over_ie_speed": round(ie_ms / (prep_ms + attn_ms), 4)}
         del iws
 
+    # decode alone, 50 back-to-back calls after the timed region (median, min)
+    dec50 = None
+    if do_decode and not args.only:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for a, b in ev:
+            a.record()
+            jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
+            b.record()
+        torch.cuda.synchronize()
+        d50 = [a.elapsed_time(b) for a, b in ev]
+        dec50 = [round(median(d50), 4), round(min(d50), 4)]
+
     cpu = None
     if not args.no_cpu_baseline and do_prefill:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
@@ -295,6 +308,9 @@ def main():
             "prefill_prepare_ms": round(prep_ms, 3),
             "prefill_attend_ms": round(attn_ms, 3),
             "decode_ms": round(dec_ms, 4),
+            "prefill_attend_ms_median_min": [round(median(attn), 3), round(min(attn), 3)] if do_prefill else None,
+            "decode_ms_median_min": [round(median(dec), 4), round(min(dec), 4)] if do_decode else None,
+            "decode_ms_median_min_50": dec50,
             "decode_GBps": round(dec_gbs, 1),
             "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
             "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4),

@@ -295,3 +295,26 @@ def test_decode_steps_across_G_boundaries(dt):
     o_sep, _ = run_decode(inp, wp, w0, theta)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), o_sep)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prepare_once_attend_several_windows(dt):
+    """One prepared workspace (rotated key copies, V^T, table) serves attends
+    with different local windows, each matching the oracle."""
+    torch = _torch()
+    L, wp, theta = 1300, 256, 1e4
+    _say("prepare once, attend twice", dt)
+    inp = W.prefill_inputs([L], 8, 2, 128, dt, 24)
+    q = W.to_device(inp["q"], dt)
+    k = W.to_device(inp["k"], dt)
+    v = W.to_device(inp["v"], dt)
+    cu = torch.from_numpy(inp["cu_q"]).cuda()
+    ws = jl.prefill_prepare(k, v, cu, L, wp, theta, Hq=8)
+    for w0 in (64, 500):
+        out, lse = jl.prefill_attend(q, k, v, cu, L, wp, w0, theta, ws, return_lse=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle_prefill(inp, wp, w0, theta)
+        eo = float(np.max(np.abs(out.float().cpu().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse.cpu().numpy().T - l_ref)))
+        _say(f"w0={w0}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= TOL[dt] and el <= TOL[dt], (w0, eo, el)
