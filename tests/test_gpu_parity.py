@@ -318,3 +318,31 @@ def test_prepare_once_attend_several_windows(dt):
         el = float(np.max(np.abs(lse.cpu().numpy().T - l_ref)))
         _say(f"w0={w0}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
         assert eo <= TOL[dt] and el <= TOL[dt], (w0, eo, el)
+
+
+def test_chunked_prefill_across_G_boundary_same_cache():
+    """Two prefill chunks over one unchanged key/value buffer: the first ends
+    at L = w_pretrained (G = 1), the second at L = w_pretrained + 150 (G = 2);
+    each attends to the cache as it stands, with G taken from its own length."""
+    torch = _torch()
+    wp, w0, theta, Hq, Hkv, d = 256, 40, 1e4, 8, 2, 128
+    Lmax = wp + 150
+    _say("chunks across G boundary")
+    full = W.prefill_inputs([Lmax], Hq, Hkv, d, "bf16", 25)
+    k = W.to_device(full["k"], "bf16")
+    v = W.to_device(full["v"], "bf16")
+    for L, Lq in ((wp, 100), (Lmax, Lmax - wp)):
+        q_np = full["q"][L - Lq:L]
+        q = W.to_device(q_np, "bf16")
+        cu_q = torch.tensor([0, Lq], dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        out, lse = jl.prefill(q, k[:L], v[:L], cu_q, Lq, wp, w0, theta, cu_seqlens_k=cu_k, max_seqlen_k=L,
+                              return_lse=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.bifocal_sequence(W.as_f64(q_np, "bf16"), W.as_f64(full["k"][:L], "bf16"),
+                                               W.as_f64(full["v"][:L], "bf16"), np.arange(L - Lq, L), L, wp, w0,
+                                               theta)
+        eo = float(np.max(np.abs(out.float().cpu().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse.cpu().numpy().T - l_ref)))
+        _say(f"L={L} (G={jl.group_size(L, wp)}): max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (L, eo, el)
