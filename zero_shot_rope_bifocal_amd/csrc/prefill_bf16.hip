@@ -233,6 +233,34 @@ __device__ __forceinline__ void store_tile(const TileRegs<D * kBN / 8 / NT>& t, 
   for (int i = 0; i < CPT; ++i) st_v(sV, tid + i * NT, t.v[i]);
 }
 
+// load_tile / store_tile for a tile class known at compile time: inside the
+// fast loops every load is unconditional, so the staging registers carry no
+// control-flow merge (whose register copies would wait for the loads at once).
+template <int D, int NT, int BASE>
+__device__ __forceinline__ void load_tile_c(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
+                                            const uint16_t* kl_base, const uint16_t* vt_base, int64_t tpad,
+                                            int64_t row0, int tid) {
+  constexpr int CPT = D * kBN / 8 / NT;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    if constexpr (BASE != kLocal) t.kr[i] = ld_k<D>(kr_base, row0, tid + i * NT);
+    if constexpr (BASE != kRemote) t.kl[i] = ld_k<D>(kl_base, row0, tid + i * NT);
+    t.v[i] = ld_v(vt_base, tpad, row0, tid + i * NT);
+  }
+}
+
+template <int D, int NT, int BASE>
+__device__ __forceinline__ void store_tile_c(const TileRegs<D * kBN / 8 / NT>& t, uint16_t* sKr, uint16_t* sKl,
+                                             uint16_t* sV, int tid) {
+  constexpr int CPT = D * kBN / 8 / NT;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    if constexpr (BASE != kLocal) st_k<D>(sKr, tid + i * NT, t.kr[i]);
+    if constexpr (BASE != kRemote) st_k<D>(sKl, tid + i * NT, t.kl[i]);
+    st_v(sV, tid + i * NT, t.v[i]);
+  }
+}
+
 // Raw bf16 query fragment of this lane (features ks*16 + g*8 + e), or zeros.
 template <int D>
 __device__ __forceinline__ void load_query(float (&x)[D / 16][8], const uint16_t* src, bool valid, int g) {
@@ -591,33 +619,44 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
   int kt = kt0;
   int ncls = 0;
   while (!BAND && kt < nrem) {
-    for (; kt < nrem; ++kt) {
+    // fast loop over tiles whose successor is all-remote as well
+    bool in_flight = false;  // loads of tile kt + 1 already issued
+    for (; kt + 1 < nrem; ++kt) {
       const int buf = kt & 1;
-      ncls = 0;
-      if (kt + 1 < nkt) {
-        ncls = cls_of(kt + 1);
-        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
-      }
+      load_tile_c<D, NT, kRemote>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN,
+                                  tid);
+      in_flight = true;
       if ((cls & kDiag) || kt * kBN + kBN > L) break;
       if (!tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run)) break;
-      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+      store_tile_c<D, NT, kRemote>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+      in_flight = false;
       __syncthreads();
-      cls = ncls;
+      cls = cls_of(kt + 1);
     }
-    if (kt < nrem) {  // the loads of tile kt + 1 are already in flight
-      const int buf = kt & 1;
+    // tile kt: one the fast path declined or that needs a mask (the loads of
+    // tile kt + 1 are in flight), or the last all-remote tile
+    const int buf = kt & 1;
+    ncls = kt + 1 < nkt ? cls_of(kt + 1) : 0;
+    const bool masked = (cls & kDiag) || kt * kBN + kBN > L;
+    bool done = false;
+    if (!in_flight) {
+      if (kt + 1 < nkt)
+        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+      if (!masked) done = tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run);
+    }
+    if (!done) {
       const int j0g = kt * kBN + g * 4;
-      if ((cls & kDiag) || kt * kBN + kBN > L)
-        tile_slow<D, NRB, true, false, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
-                                             acc, m_run, l_run, qi, j0g, L, p.w0);
+      if (masked)
+        tile_slow<D, NRB, true, false, true>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
+                                             m_run, l_run, qi, j0g, L, p.w0);
       else
-        tile_slow<D, NRB, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf,
-                                              acc, m_run, l_run, qi, j0g, L, p.w0);
-      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
-      __syncthreads();
-      cls = ncls;
-      ++kt;
+        tile_slow<D, NRB, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
+                                              m_run, l_run, qi, j0g, L, p.w0);
     }
+    if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+    __syncthreads();
+    cls = ncls;
+    ++kt;
   }
 
   // ---- window-edge and local tiles: the local query joins (slow path)
@@ -665,34 +704,37 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     // all-local tiles: one rotation again, so the fast path as for the
     // remote tiles (only the local query is live from here on)
     while (kt < nkt) {
-      for (; kt < nkt; ++kt) {
+      bool in_flight = false;
+      for (; kt + 1 < nkt; ++kt) {
         const int buf = kt & 1;
-        ncls = 0;
-        if (kt + 1 < nkt) {
-          ncls = cls_of(kt + 1);
-          load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls,
-                           tid);
-        }
+        load_tile_c<D, NT, kLocal>(tr, kr_base, kl_base, vt_base, p.tpad,
+                                   krow0 + static_cast<int64_t>(kt + 1) * kBN, tid);
+        in_flight = true;
         if ((cls & kDiag) || kt * kBN + kBN > L) break;
         if (!tile_fast<D, NRB>(sKl[buf] + kr_off, sV[buf] + v_off, qlf, acc, m_run, l_run)) break;
-        if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+        store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+        in_flight = false;
         __syncthreads();
-        cls = ncls;
+        cls = cls_of(kt + 1);
       }
-      if (kt < nkt) {  // the loads of tile kt + 1 are already in flight
-        const int buf = kt & 1;
+      const int buf = kt & 1;
+      ncls = kt + 1 < nkt ? cls_of(kt + 1) : 0;
+      const bool masked = (cls & kDiag) || kt * kBN + kBN > L;
+      bool done = false;
+      if (!in_flight && !masked) done = tile_fast<D, NRB>(sKl[buf] + kr_off, sV[buf] + v_off, qlf, acc, m_run, l_run);
+      if (!done) {
         const int j0g = kt * kBN + g * 4;
-        if ((cls & kDiag) || kt * kBN + kBN > L)
+        if (masked)
           tile_slow<D, NRB, false, true, true, BAND ? kPairsWindow : kPairsAll>(
               sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
         else
           tile_slow<D, NRB, false, true, false, BAND ? kPairsWindow : kPairsAll>(
               sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
-        if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
-        __syncthreads();
-        cls = ncls;
-        ++kt;
       }
+      if (kt + 1 < nkt) store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+      __syncthreads();
+      cls = ncls;
+      ++kt;
     }
   }
 
