@@ -305,24 +305,35 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 }
 
 // P^T (half) from log2-domain scores already relative to the row's running
-// max; returns the row sum of the rounded probabilities (they are what P V
-// multiplies).
-__device__ __forceinline__ float probs(const float (&t)[2][16], f16x8 (&pf)[4]) {
+// max; returns this lane's sum of the rounded probabilities (they are what
+// P V multiplies), as a pairwise tree of packed half adds.  The tree is cheap
+// next to the other wavefront's MFMAs (the f16 dot instructions that would
+// sum in fp32 share the matrix pipeline and stall behind them); each level
+// rounds to half, a relative error below 2^-11 per level, unbiased, against
+// the bf16 rounding of the output.  The caller keeps every probability
+// below 2^8, so the 32 terms cannot overflow half.
+__device__ __forceinline__ float lane_probs(const float (&t)[2][16], f16x8 (&pf)[4]) {
 #pragma unroll
   for (int ks2 = 0; ks2 < 4; ++ks2)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       pf[ks2][e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(t[ks2 >> 1][(ks2 & 1) * 8 + e]));
-  const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-  float rs = 0.f;
+  f16x2 h[8];
 #pragma unroll
-  for (int ks2 = 0; ks2 < 4; ++ks2)
+  for (int i = 0; i < 8; ++i) {
+    const f16x2 a = {pf[i >> 1][(i & 1) * 4 + 0], pf[i >> 1][(i & 1) * 4 + 1]};
+    const f16x2 b = {pf[i >> 1][(i & 1) * 4 + 2], pf[i >> 1][(i & 1) * 4 + 3]};
+    h[i] = a + b;
+  }
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const f16x2 pr = {pf[ks2][e], pf[ks2][e + 1]};
-      rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-    }
-  return xhalf_sum(rs);
+  for (int st = 4; st >= 1; st >>= 1)
+#pragma unroll
+    for (int i = 0; i < st; ++i) h[i] = h[i] + h[i + st];
+  return static_cast<float>(h[0][0]) + static_cast<float>(h[0][1]);
+}
+// Row sum of P^T (both lane halves).
+__device__ __forceinline__ float probs(const float (&t)[2][16], f16x8 (&pf)[4]) {
+  return xhalf_sum(lane_probs(t, pf));
 }
 
 // O^T += V^T P^T for NRB row blocks: every V^T fragment (one 16-byte LDS read:
@@ -402,10 +413,12 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
 
 // Fast path of an unmasked tile scored with one rotation (all-remote, or
 // all-local with the local rotations).  The score accumulators start at
-// -m_run, so they come out relative to the running max.  If any row's max
-// rose by more than 8 (log2) the tile is left to the slow path and nothing is
-// changed; otherwise the stale max stands (probabilities stay below 2^8, far
-// inside half range) and no rescale of O is needed.
+// -m_run, so they come out relative to the running max and the
+// probabilities follow at once.  If any lane's sum of them exceeds 2^8 (so
+// some row's max may have risen by more than 8, log2; an infinite or NaN sum
+// included) the tile is left to the slow path, which recomputes it, and
+// nothing is changed.  Otherwise every probability is below 2^8, far inside
+// half range, the stale max stands and O needs no rescale.
 template <int D, int NRB>
 __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ v_lane,
@@ -416,18 +429,9 @@ __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
   for (int rb = 0; rb < NRB; ++rb) init[rb] = -m_run[rb];
   f32x16 sc[NRB][2];
   qk<D, NRB>(kr_lane, qrf, init, sc);
-  bool grow = false;
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    float mx = sc[rb][0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
-    grow = grow || xhalf_max(mx) > 8.f;
-  }
-  if (__any(grow)) return false;
   f16x8 pf[NRB][4];
+  float ls[NRB];
+  bool grow = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float t[2][16];
@@ -435,8 +439,12 @@ __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[kb][r] = sc[rb][kb][r];
-    l_run[rb] += probs(t, pf[rb]);
+    ls[rb] = lane_probs(t, pf[rb]);
+    grow = grow || !(ls[rb] <= 256.f);
   }
+  if (__any(grow)) return false;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) l_run[rb] += xhalf_sum(ls[rb]);
   pv<D, NRB>(v_lane, pf, acc);
   return true;
 }
