@@ -11,9 +11,11 @@
 // Two kernels per call, both on the caller's stream:
 //  1. prep: every key row is rotated once at its true position p and once at
 //     f(p) (head-major rows padded per sequence to a multiple of 64) and V is
-//     laid out transposed per head, [d][key], with each 16-key group in the
-//     k-slot order of the PV MFMA, so that one A fragment (8 keys of one
-//     feature) is one 16-byte LDS read.  The raw K/V inputs are only read.
+//     laid out transposed per head and 64-key tile, [tile][d][64 keys], with
+//     each 16-key group in the k-slot order of the PV MFMA, so that one A
+//     fragment (8 keys of one feature) is one 16-byte LDS read.  Every K and
+//     V^T tile is then one contiguous 64 x d block.  The raw K/V inputs are
+//     only read.
 //  Operand precision: the MFMA operands (rotated Q and K, P, V) are IEEE
 //  half, accumulation is fp32.  bf16 inputs convert to half exactly (within
 //  +-65504), and rotation keeps each pair's norm, while a rotated value
@@ -50,7 +52,7 @@ struct Params {
   const float2* tab;  // [max_k][D/2]
   uint16_t* kr;       // [Hkv][tpad][D]  keys rotated at f(p), half
   uint16_t* kl;       // [Hkv][tpad][D]  keys rotated at p, half
-  uint16_t* vt;       // [Hkv][D][tpad]  values, transposed, half
+  uint16_t* vt;       // [Hkv][tpad / 64][D][64]  values, transposed per 64-key tile, half
   int64_t tpad;
   int B, total_q, Hq, Hkv, ratio, ngroups, nqb, max_q, max_k;
   int w_pretrained, w0;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
   // the order 0, 2, 1, 3, which is the order the PV MFMA's k slots take them
   const int64_t rq = (r >> 2) & 3;
   const int64_t vcol = (r & ~15LL) | (((rq == 1) ? 2 : (rq == 2) ? 1 : rq) << 2) | (r & 3);
-  uint16_t* vt_col = p.vt + static_cast<int64_t>(hk) * D * p.tpad + vcol;
+  uint16_t* vt_col = p.vt + static_cast<int64_t>(hk) * D * p.tpad + (r >> 6) * (D * 64) + (vcol & 63);
   if (pos < L) {
     const int64_t tok = p.cu_k[b] + pos;
     const int G = group_size(L, p.w_pretrained);
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float x = bf16_bits_to_float(static_cast<uint16_t>(vv[e >> 1] >> (16 * (e & 1))));
-      vt_col[static_cast<int64_t>(c * 16 + e) * p.tpad] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+      vt_col[(c * 16 + e) * 64] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
     }
   } else {
     const uint4 z = make_uint4(0, 0, 0, 0);
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
     *reinterpret_cast<uint4*>(kr_row + c * 8) = z;
     *reinterpret_cast<uint4*>(kr_row + H + c * 8) = z;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) vt_col[static_cast<int64_t>(c * 16 + e) * p.tpad] = 0;
+    for (int e = 0; e < 16; ++e) vt_col[(c * 16 + e) * 64] = 0;
   }
 }
 
@@ -174,14 +176,10 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 
 constexpr int kVSTR = kBN + 8;  // LDS row stride of V^T tiles (elements, 16-byte rows)
 
-// chunk c of a key tile: row c / (D/8), 16-byte column c % (D/8)
-template <int D>
-__device__ __forceinline__ uint4 ld_k(const uint16_t* base, int64_t row0, int c) {
-  return *reinterpret_cast<const uint4*>(base + (row0 + c / (D / 8)) * D + (c % (D / 8)) * 8);
-}
-// chunk c of a V^T tile: feature row c / 8, 16-byte column c % 8
-__device__ __forceinline__ uint4 ld_v(const uint16_t* base, int64_t tpad, int64_t row0, int c) {
-  return *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(c / (kBN / 8)) * tpad + row0 + (c % (kBN / 8)) * 8);
+// 16-byte chunk c of a contiguous 64-key tile (K: row c / (D/8), column
+// c % (D/8); V^T: feature row c / 8, column c % 8).
+__device__ __forceinline__ uint4 ld_chunk(const uint16_t* tile, int c) {
+  return *reinterpret_cast<const uint4*>(tile + c * 8);
 }
 template <int D>
 __device__ __forceinline__ void st_k(uint16_t* s, int c, uint4 val) {
@@ -200,20 +198,20 @@ struct TileRegs {
 
 template <int D, int NT>
 __device__ __forceinline__ void load_tile(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
-                                          const uint16_t* kl_base, const uint16_t* vt_base, int64_t tpad,
+                                          const uint16_t* kl_base, const uint16_t* vt_base,
                                           int64_t row0, int cls, int tid) {
   constexpr int CPT = D * kBN / 8 / NT;
   const int base = cls & 3;
   if (base != kLocal) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) t.kr[i] = ld_k<D>(kr_base, row0, tid + i * NT);
+    for (int i = 0; i < CPT; ++i) t.kr[i] = ld_chunk(kr_base + row0 * D, tid + i * NT);
   }
   if (base != kRemote) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) t.kl[i] = ld_k<D>(kl_base, row0, tid + i * NT);
+    for (int i = 0; i < CPT; ++i) t.kl[i] = ld_chunk(kl_base + row0 * D, tid + i * NT);
   }
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) t.v[i] = ld_v(vt_base, tpad, row0, tid + i * NT);
+  for (int i = 0; i < CPT; ++i) t.v[i] = ld_chunk(vt_base + row0 * D, tid + i * NT);
 }
 
 template <int D, int NT>
@@ -238,14 +236,14 @@ __device__ __forceinline__ void store_tile(const TileRegs<D * kBN / 8 / NT>& t, 
 // control-flow merge (whose register copies would wait for the loads at once).
 template <int D, int NT, int BASE>
 __device__ __forceinline__ void load_tile_c(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
-                                            const uint16_t* kl_base, const uint16_t* vt_base, int64_t tpad,
+                                            const uint16_t* kl_base, const uint16_t* vt_base,
                                             int64_t row0, int tid) {
   constexpr int CPT = D * kBN / 8 / NT;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    if constexpr (BASE != kLocal) t.kr[i] = ld_k<D>(kr_base, row0, tid + i * NT);
-    if constexpr (BASE != kRemote) t.kl[i] = ld_k<D>(kl_base, row0, tid + i * NT);
-    t.v[i] = ld_v(vt_base, tpad, row0, tid + i * NT);
+    if constexpr (BASE != kLocal) t.kr[i] = ld_chunk(kr_base + row0 * D, tid + i * NT);
+    if constexpr (BASE != kRemote) t.kl[i] = ld_chunk(kl_base + row0 * D, tid + i * NT);
+    t.v[i] = ld_chunk(vt_base + row0 * D, tid + i * NT);
   }
 }
 
@@ -609,12 +607,12 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     cls = 0;
     if (kt0 < nkt) {
       cls = cls_of(kt0);
-      load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt0) * kBN, cls, tid);
+      load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt0) * kBN, cls, tid);
       store_tile<D, NT>(tr, sKr[kt0 & 1], sKl[kt0 & 1], sV[kt0 & 1], cls, tid);
     }
   } else {
     cls = cls_of(0);
-    load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0, cls, tid);
+    load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0, cls, tid);
     store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tid);
   }
   __syncthreads();
@@ -631,7 +629,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     bool in_flight = false;  // loads of tile kt + 1 already issued
     for (; kt + 1 < nrem; ++kt) {
       const int buf = kt & 1;
-      load_tile_c<D, NT, kRemote>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN,
+      load_tile_c<D, NT, kRemote>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN,
                                   tid);
       in_flight = true;
       if ((cls & kDiag) || kt * kBN + kBN > L) break;
@@ -649,7 +647,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     bool done = false;
     if (!in_flight) {
       if (kt + 1 < nkt)
-        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
       if (!masked) done = tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run);
     }
     if (!done) {
@@ -686,7 +684,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       ncls = 0;
       if (kt + 1 < nkt) {
         ncls = cls_of(kt + 1);
-        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, p.tpad, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
       }
       const int j0g = kt * kBN + g * 4;
       const uint16_t* krl = sKr[buf] + kr_off;
@@ -715,7 +713,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       bool in_flight = false;
       for (; kt + 1 < nkt; ++kt) {
         const int buf = kt & 1;
-        load_tile_c<D, NT, kLocal>(tr, kr_base, kl_base, vt_base, p.tpad,
+        load_tile_c<D, NT, kLocal>(tr, kr_base, kl_base, vt_base,
                                    krow0 + static_cast<int64_t>(kt + 1) * kBN, tid);
         in_flight = true;
         if ((cls & kDiag) || kt * kBN + kBN > L) break;
