@@ -37,7 +37,10 @@
  *             output).  Accumulation, softmax and rotation run in fp32; the
  *             RoPE angles and their cos/sin are formed in fp64.
  *   head_dim: 64 or 128.  Hq must be a multiple of Hkv.
- *   Limits:   sequence lengths < 2^31; positions are int32.
+ *   Limits:   sequence lengths < 2^31; positions are int32.  bf16 prefill
+ *             (prepare and attend): (roundup64(total_k) + 64 B) * head_dim
+ *             * 2 must not exceed 2^31 - 1 (about 8.4M keys per call at
+ *             head_dim 128), else JL_ERR_UNSUPPORTED.
  */
 #ifndef JETLONG_H
 #define JETLONG_H
@@ -52,7 +55,7 @@ extern "C" {
 typedef enum {
   JL_OK = 0,
   JL_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % Hkv != 0 ... */
-  JL_ERR_UNSUPPORTED = -2, /* head_dim or dtype outside the supported set   */
+  JL_ERR_UNSUPPORTED = -2, /* head_dim, dtype or size outside what is built */
   JL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required    */
   JL_ERR_HIP = -4          /* a HIP call failed (launch, device query)      */
 } jl_status;

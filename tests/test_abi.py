@@ -63,6 +63,21 @@ def test_prefill_rejects_before_any_launch(kw, code):
     assert L.jl_last_error().decode() != ""
 
 
+def test_prefill_bf16_key_span_limit():
+    # bf16 tiles are addressed with 31-bit byte offsets per KV head:
+    # (roundup64(total_k) + 64 B) * d * 2 <= 2^31 - 1
+    L = _lib()
+    big = dict(total_k=1 << 23, max_k=64, cu_k=1)
+    assert _prefill(L, **big) == -2
+    assert "2^31" in L.jl_last_error().decode()
+    # just inside the limit the call gets past the check (and stops at the missing workspace)
+    assert _prefill(L, total_k=(1 << 23) - 128, max_k=64, cu_k=1, ws=None) == -3
+    # fp32 does not use these tiles
+    assert _prefill(L, dtype=jl.JL_F32, ws=None, **big) == -3
+    # head_dim 64 halves the bytes per key
+    assert _prefill(L, d=64, ws=None, **big) == -3
+
+
 def test_prefill_empty_batch_is_ok():
     L = _lib()
     assert _prefill(L, B=0, q=None, k=None, v=None, o=None, cu_q=None, ws=None) == 0

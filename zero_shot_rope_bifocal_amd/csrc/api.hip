@@ -3,6 +3,7 @@
 // Every argument is checked before any HIP call; a failing call enqueues
 // nothing and leaves a message for jl_last_error() on the calling thread.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -82,6 +83,18 @@ namespace {
 
 // Checks a full prefill argument list and fills `c`; JL_OK with c.B == 0 or
 // c.total_q == 0 means there is nothing to launch.
+// bf16 prefill: the attention kernel addresses one KV head's rotated keys
+// and V^T tiles with 32-bit byte offsets below 2^31, i.e. padded keys
+// (roundup64(total_k) + 64 B) times 2 head_dim bytes.
+int check_bf16_key_span(int dtype, int B, int total_k, int head_dim) {
+  if (dtype != JL_BF16) return JL_OK;
+  const int64_t tpad = (static_cast<int64_t>(total_k) + 63) / 64 * 64 + 64LL * B;
+  if (tpad * head_dim * 2 > INT32_MAX)
+    return fail(JL_ERR_UNSUPPORTED, "bf16 prefill of %lld padded keys x head_dim %d exceeds 2^31 bytes per KV head",
+                static_cast<long long>(tpad), head_dim);
+  return JL_OK;
+}
+
 int prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
                  int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int head_dim,
@@ -95,6 +108,8 @@ int prefill_args(const void* q, const void* k, const void* v, void* o, float* ls
   if (total_q > total_k) return fail(JL_ERR_INVALID_ARG, "total_q=%d exceeds total_k=%d", total_q, total_k);
   if (max_seqlen_q > max_seqlen_k) return fail(JL_ERR_INVALID_ARG, "max_seqlen_q exceeds max_seqlen_k");
   if (B == 0 || total_q == 0) return JL_OK;
+  st = check_bf16_key_span(dtype, B, total_k, head_dim);
+  if (st != JL_OK) return st;
   if (!q || !k || !v || !o) return fail(JL_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   if (!cu_seqlens_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_q must be non-null");
   if (!cu_seqlens_k && total_k != total_q) return fail(JL_ERR_INVALID_ARG, "cu_seqlens_k is NULL but total_k != total_q");
@@ -166,6 +181,8 @@ int jl_bifocal_prefill_prepare_ex(const void* k, const void* v, int dtype, const
   if (st != JL_OK) return st;
   if (B < 0 || total_k < 0 || max_seqlen_k < 0) return fail(JL_ERR_INVALID_ARG, "sizes must be non-negative");
   if (B == 0 || total_k == 0) return JL_OK;
+  st = check_bf16_key_span(dtype, B, total_k, head_dim);
+  if (st != JL_OK) return st;
   if (!k || !v || !cu_seqlens_k) return fail(JL_ERR_INVALID_ARG, "k, v and cu_seqlens_k must be non-null");
   if (max_seqlen_k < 1) return fail(JL_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 for a non-empty batch");
   const size_t need = jl_bifocal_prefill_workspace_size(dtype, B, total_k, max_seqlen_k, Hkv, Hkv, head_dim);

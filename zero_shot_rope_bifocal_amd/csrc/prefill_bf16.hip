@@ -176,19 +176,6 @@ __global__ __launch_bounds__(64) void prep_kernel(Params p) {
 
 constexpr int kVSTR = kBN + 8;  // LDS row stride of V^T tiles (elements, 16-byte rows)
 
-// 16-byte chunk c of a contiguous 64-key tile (K: row c / (D/8), column
-// c % (D/8); V^T: feature row c / 8, column c % 8).
-__device__ __forceinline__ uint4 ld_chunk(const uint16_t* tile, int c) {
-  return *reinterpret_cast<const uint4*>(tile + c * 8);
-}
-template <int D>
-__device__ __forceinline__ void st_k(uint16_t* s, int c, uint4 val) {
-  *reinterpret_cast<uint4*>(s + (c / (D / 8)) * (D + 8) + (c % (D / 8)) * 8) = val;
-}
-__device__ __forceinline__ void st_v(uint16_t* s, int c, uint4 val) {
-  *reinterpret_cast<uint4*>(s + (c / (kBN / 8)) * kVSTR + (c % (kBN / 8)) * 8) = val;
-}
-
 // Per-thread registers of one prefetched tile (global -> registers -> LDS):
 // CPT 16-byte chunks of each of K (remote), K (local) and V^T.
 template <int CPT>
@@ -196,66 +183,96 @@ struct TileRegs {
   uint4 kr[CPT], kl[CPT], v[CPT];
 };
 
+// Where one lane's part of a tile comes from and goes: buffer resources over
+// one KV head's rotated key copies and V^T tiles (the tile's byte offset is
+// a scalar, the lane's byte offset inside the tile a constant), and the
+// lane's element offsets inside an LDS key / V^T tile.  Lane tid moves the
+// CPT consecutive chunks tid*CPT .. (always inside one LDS row).
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t kr, kl, vt;
+  uint32_t voff;  // bytes
+  uint32_t lk, lv;  // LDS elements
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 template <int D, int NT>
-__device__ __forceinline__ void load_tile(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
-                                          const uint16_t* kl_base, const uint16_t* vt_base,
-                                          int64_t row0, int cls, int tid) {
+__device__ __forceinline__ TileSrc tile_src(const uint16_t* kr_base, const uint16_t* kl_base, const uint16_t* vt_base,
+                                            int64_t tpad, int tid) {
+  constexpr int CPT = D * kBN / 8 / NT;
+  const int c0 = tid * CPT;
+  TileSrc s;
+  s.kr = head_rsrc(kr_base, tpad * D * 2);
+  s.kl = head_rsrc(kl_base, tpad * D * 2);
+  s.vt = head_rsrc(vt_base, tpad * D * 2);
+  s.voff = static_cast<uint32_t>(c0) * 16u;
+  s.lk = static_cast<uint32_t>((c0 / (D / 8)) * (D + 8) + (c0 % (D / 8)) * 8);
+  s.lv = static_cast<uint32_t>((c0 / (kBN / 8)) * kVSTR + (c0 % (kBN / 8)) * 8);
+  return s;
+}
+template <int D>
+__device__ __forceinline__ uint32_t tile_soff(int64_t row0) { return static_cast<uint32_t>(row0 * (D * 2)); }
+
+template <int D, int NT>
+__device__ __forceinline__ void load_tile(TileRegs<D * kBN / 8 / NT>& t, const TileSrc& s, uint32_t soff, int cls) {
   constexpr int CPT = D * kBN / 8 / NT;
   const int base = cls & 3;
   if (base != kLocal) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) t.kr[i] = ld_chunk(kr_base + row0 * D, tid + i * NT);
+    for (int i = 0; i < CPT; ++i) t.kr[i] = buf16(s.kr, s.voff + i * 16, soff);
   }
   if (base != kRemote) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) t.kl[i] = ld_chunk(kl_base + row0 * D, tid + i * NT);
+    for (int i = 0; i < CPT; ++i) t.kl[i] = buf16(s.kl, s.voff + i * 16, soff);
   }
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) t.v[i] = ld_chunk(vt_base + row0 * D, tid + i * NT);
+  for (int i = 0; i < CPT; ++i) t.v[i] = buf16(s.vt, s.voff + i * 16, soff);
 }
 
 template <int D, int NT>
 __device__ __forceinline__ void store_tile(const TileRegs<D * kBN / 8 / NT>& t, uint16_t* sKr, uint16_t* sKl,
-                                           uint16_t* sV, int cls, int tid) {
+                                           uint16_t* sV, int cls, const TileSrc& s) {
   constexpr int CPT = D * kBN / 8 / NT;
   const int base = cls & 3;
   if (base != kLocal) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) st_k<D>(sKr, tid + i * NT, t.kr[i]);
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(sKr + s.lk + i * 8) = t.kr[i];
   }
   if (base != kRemote) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) st_k<D>(sKl, tid + i * NT, t.kl[i]);
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(sKl + s.lk + i * 8) = t.kl[i];
   }
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) st_v(sV, tid + i * NT, t.v[i]);
+  for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(sV + s.lv + i * 8) = t.v[i];
 }
 
 // load_tile / store_tile for a tile class known at compile time: inside the
 // fast loops every load is unconditional, so the staging registers carry no
 // control-flow merge (whose register copies would wait for the loads at once).
 template <int D, int NT, int BASE>
-__device__ __forceinline__ void load_tile_c(TileRegs<D * kBN / 8 / NT>& t, const uint16_t* kr_base,
-                                            const uint16_t* kl_base, const uint16_t* vt_base,
-                                            int64_t row0, int tid) {
+__device__ __forceinline__ void load_tile_c(TileRegs<D * kBN / 8 / NT>& t, const TileSrc& s, uint32_t soff) {
   constexpr int CPT = D * kBN / 8 / NT;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    if constexpr (BASE != kLocal) t.kr[i] = ld_chunk(kr_base + row0 * D, tid + i * NT);
-    if constexpr (BASE != kRemote) t.kl[i] = ld_chunk(kl_base + row0 * D, tid + i * NT);
-    t.v[i] = ld_chunk(vt_base + row0 * D, tid + i * NT);
+    if constexpr (BASE != kLocal) t.kr[i] = buf16(s.kr, s.voff + i * 16, soff);
+    if constexpr (BASE != kRemote) t.kl[i] = buf16(s.kl, s.voff + i * 16, soff);
+    t.v[i] = buf16(s.vt, s.voff + i * 16, soff);
   }
 }
 
 template <int D, int NT, int BASE>
 __device__ __forceinline__ void store_tile_c(const TileRegs<D * kBN / 8 / NT>& t, uint16_t* sKr, uint16_t* sKl,
-                                             uint16_t* sV, int tid) {
+                                             uint16_t* sV, const TileSrc& s) {
   constexpr int CPT = D * kBN / 8 / NT;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    if constexpr (BASE != kLocal) st_k<D>(sKr, tid + i * NT, t.kr[i]);
-    if constexpr (BASE != kRemote) st_k<D>(sKl, tid + i * NT, t.kl[i]);
-    st_v(sV, tid + i * NT, t.v[i]);
+    if constexpr (BASE != kLocal) *reinterpret_cast<uint4*>(sKr + s.lk + i * 8) = t.kr[i];
+    if constexpr (BASE != kRemote) *reinterpret_cast<uint4*>(sKl + s.lk + i * 8) = t.kl[i];
+    *reinterpret_cast<uint4*>(sV + s.lv + i * 8) = t.v[i];
   }
 }
 
@@ -580,6 +597,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
   const uint16_t* kr_base = p.kr + static_cast<int64_t>(hkv) * p.tpad * D;
   const uint16_t* kl_base = p.kl + static_cast<int64_t>(hkv) * p.tpad * D;
   const uint16_t* vt_base = p.vt + static_cast<int64_t>(hkv) * D * p.tpad;
+  const TileSrc tsrc = tile_src<D, NT>(kr_base, kl_base, vt_base, p.tpad, tid);
   const int kr_off = r32 * KSTR + g * 8;
   const int v_off = r32 * kVSTR + g * 8;
 
@@ -607,13 +625,13 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     cls = 0;
     if (kt0 < nkt) {
       cls = cls_of(kt0);
-      load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt0) * kBN, cls, tid);
-      store_tile<D, NT>(tr, sKr[kt0 & 1], sKl[kt0 & 1], sV[kt0 & 1], cls, tid);
+      load_tile<D, NT>(tr, tsrc, tile_soff<D>(krow0 + static_cast<int64_t>(kt0) * kBN), cls);
+      store_tile<D, NT>(tr, sKr[kt0 & 1], sKl[kt0 & 1], sV[kt0 & 1], cls, tsrc);
     }
   } else {
     cls = cls_of(0);
-    load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0, cls, tid);
-    store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tid);
+    load_tile<D, NT>(tr, tsrc, tile_soff<D>(krow0), cls);
+    store_tile<D, NT>(tr, sKr[0], sKl[0], sV[0], cls, tsrc);
   }
   __syncthreads();
 
@@ -629,12 +647,11 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     bool in_flight = false;  // loads of tile kt + 1 already issued
     for (; kt + 1 < nrem; ++kt) {
       const int buf = kt & 1;
-      load_tile_c<D, NT, kRemote>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN,
-                                  tid);
+      load_tile_c<D, NT, kRemote>(tr, tsrc, tile_soff<D>(krow0 + static_cast<int64_t>(kt + 1) * kBN));
       in_flight = true;
       if ((cls & kDiag) || kt * kBN + kBN > L) break;
       if (!tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run)) break;
-      store_tile_c<D, NT, kRemote>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+      store_tile_c<D, NT, kRemote>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tsrc);
       in_flight = false;
       __syncthreads();
       cls = cls_of(kt + 1);
@@ -647,7 +664,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
     bool done = false;
     if (!in_flight) {
       if (kt + 1 < nkt)
-        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        load_tile<D, NT>(tr, tsrc, tile_soff<D>(krow0 + static_cast<int64_t>(kt + 1) * kBN), ncls);
       if (!masked) done = tile_fast<D, NRB>(sKr[buf] + kr_off, sV[buf] + v_off, qrf, acc, m_run, l_run);
     }
     if (!done) {
@@ -659,7 +676,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         tile_slow<D, NRB, true, false, false>(sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc,
                                               m_run, l_run, qi, j0g, L, p.w0);
     }
-    if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+    if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tsrc);
     __syncthreads();
     cls = ncls;
     ++kt;
@@ -684,7 +701,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       ncls = 0;
       if (kt + 1 < nkt) {
         ncls = cls_of(kt + 1);
-        load_tile<D, NT>(tr, kr_base, kl_base, vt_base, krow0 + static_cast<int64_t>(kt + 1) * kBN, ncls, tid);
+        load_tile<D, NT>(tr, tsrc, tile_soff<D>(krow0 + static_cast<int64_t>(kt + 1) * kBN), ncls);
       }
       const int j0g = kt * kBN + g * 4;
       const uint16_t* krl = sKr[buf] + kr_off;
@@ -703,7 +720,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         else
           tile_slow<D, NRB, true, true, false>(krl, kll, vl, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       }
-      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tid);
+      if (kt + 1 < nkt) store_tile<D, NT>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], ncls, tsrc);
       __syncthreads();
       cls = ncls;
     }
@@ -713,12 +730,11 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
       bool in_flight = false;
       for (; kt + 1 < nkt; ++kt) {
         const int buf = kt & 1;
-        load_tile_c<D, NT, kLocal>(tr, kr_base, kl_base, vt_base,
-                                   krow0 + static_cast<int64_t>(kt + 1) * kBN, tid);
+        load_tile_c<D, NT, kLocal>(tr, tsrc, tile_soff<D>(krow0 + static_cast<int64_t>(kt + 1) * kBN));
         in_flight = true;
         if ((cls & kDiag) || kt * kBN + kBN > L) break;
         if (!tile_fast<D, NRB>(sKl[buf] + kr_off, sV[buf] + v_off, qlf, acc, m_run, l_run)) break;
-        store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+        store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tsrc);
         in_flight = false;
         __syncthreads();
         cls = cls_of(kt + 1);
@@ -737,7 +753,7 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
           tile_slow<D, NRB, false, true, false, BAND ? kPairsWindow : kPairsAll>(
               sKr[buf] + kr_off, sKl[buf] + kr_off, sV[buf] + v_off, qrf, qlf, acc, m_run, l_run, qi, j0g, L, p.w0);
       }
-      if (kt + 1 < nkt) store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tid);
+      if (kt + 1 < nkt) store_tile_c<D, NT, kLocal>(tr, sKr[buf ^ 1], sKl[buf ^ 1], sV[buf ^ 1], tsrc);
       __syncthreads();
       cls = ncls;
       ++kt;
