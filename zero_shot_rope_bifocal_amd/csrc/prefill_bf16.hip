@@ -325,8 +325,9 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // next to the other wavefront's MFMAs (the f16 dot instructions that would
 // sum in fp32 share the matrix pipeline and stall behind them); each level
 // rounds to half, a relative error below 2^-11 per level, unbiased, against
-// the bf16 rounding of the output.  The caller keeps every probability
-// below 2^8, so the 32 terms cannot overflow half.
+// the bf16 rounding of the output.  A sum that overflows half comes out
+// infinite, which the fast path's check catches; on the slow path every
+// probability is at most 1.
 __device__ __forceinline__ float lane_probs(const float (&t)[2][16], f16x8 (&pf)[4]) {
 #pragma unroll
   for (int ks2 = 0; ks2 < 4; ++ks2)
@@ -429,11 +430,12 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ k_lane, const f1
 // Fast path of an unmasked tile scored with one rotation (all-remote, or
 // all-local with the local rotations).  The score accumulators start at
 // -m_run, so they come out relative to the running max and the
-// probabilities follow at once.  If any lane's sum of them exceeds 2^8 (so
-// some row's max may have risen by more than 8, log2; an infinite or NaN sum
+// probabilities follow at once.  If any lane's sum of them exceeds 2^12
+// (some row's max may have risen by 7 or more, log2; an infinite or NaN sum
 // included) the tile is left to the slow path, which recomputes it, and
-// nothing is changed.  Otherwise every probability is below 2^8, far inside
-// half range, the stale max stands and O needs no rescale.
+// nothing is changed.  Otherwise every probability and partial sum is at
+// most 2^12, well inside half range (half keeps its relative precision at
+// any magnitude), the stale max stands and O needs no rescale.
 template <int D, int NRB>
 __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
                                           const uint16_t* __restrict__ v_lane,
@@ -455,7 +457,7 @@ __device__ __forceinline__ bool tile_fast(const uint16_t* __restrict__ kr_lane,
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[kb][r] = sc[rb][kb][r];
     ls[rb] = lane_probs(t, pf[rb]);
-    grow = grow || !(ls[rb] <= 256.f);
+    grow = grow || !(ls[rb] <= 4096.f);
   }
   if (__any(grow)) return false;
 #pragma unroll
