@@ -79,14 +79,16 @@ __device__ __forceinline__ int64_t key_row_offset(const int32_t* cu_k, int b) {
 }
 
 // ---------------------------------------------------------------- prep pass
-// grid (tpad / 64, Hkv, D / 16), 64 threads; thread = one padded key row and
-// one 1/(D/16) slice of the features.
+// grid (tpad / 64, Hkv), 4 * D threads: a workgroup covers 64 padded key
+// rows of one KV head; wavefront c takes one 1/(D/16) slice of the features
+// of every row (lane = row), so the D/16 slices of a row are read and
+// written together.
 template <int D>
-__global__ __launch_bounds__(64) void prep_kernel(Params p) {
+__global__ __launch_bounds__(4 * D) void prep_kernel(Params p) {
   constexpr int H = D / 2;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
   const int hk = blockIdx.y;
-  const int c = blockIdx.z;  // K: elements c*8..+7 and H+c*8..+7; V: c*16..+15
+  const int c = threadIdx.x >> 6;  // K: elements c*8..+7 and H+c*8..+7; V: c*16..+15
   if (r >= p.tpad) return;
   int lo = 0, hi = p.B - 1;
   while (lo < hi) {
@@ -891,9 +893,9 @@ hipError_t launch_prefill_bf16_prepare(const PrefillCall& c, hipStream_t s) {
   const Params p = make_params(c);
   hipError_t e = launch_rope_table(static_cast<float2*>(c.ws), c.max_k, c.D, c.theta, s);
   if (e != hipSuccess) return e;
-  const dim3 pg(static_cast<unsigned>((p.tpad + 63) / 64), c.Hkv, c.D / 16);
-  if (c.D == 128) hipLaunchKernelGGL(prep_kernel<128>, pg, dim3(64), 0, s, p);
-  else hipLaunchKernelGGL(prep_kernel<64>, pg, dim3(64), 0, s, p);
+  const dim3 pg(static_cast<unsigned>((p.tpad + 63) / 64), c.Hkv);
+  if (c.D == 128) hipLaunchKernelGGL(prep_kernel<128>, pg, dim3(4 * 128), 0, s, p);
+  else hipLaunchKernelGGL(prep_kernel<64>, pg, dim3(4 * 64), 0, s, p);
   return hipGetLastError();
 }
 
