@@ -170,6 +170,27 @@ def test_prefill_peaked_keys():
     check_prefill(inp, 512, 128, 1e6)
 
 
+@pytest.mark.parametrize("rise", [6.0, 16.0])  # log2 climb ~ rise * 8 / sqrt(128) / ln 2
+def test_prefill_rising_scores(rise):
+    """Scores that climb along the keys of every row: one feature of the
+    lowest-frequency rotation pair (features d/2 - 1 and d - 1, nearly
+    position-independent over 2048 keys) carries a query weight of 8 and a
+    key weight growing linearly to `rise` (a total climb of about 6 or 16
+    log2 units), so each row's maximum rises tile after tile by a fraction
+    of a log2 unit.  The fast path then keeps a
+    stale maximum over many tiles with probabilities far above 1 before the
+    slow path rescales; the result must still match the oracle."""
+    _torch()
+    _say("rising scores", rise)
+    inp = W.prefill_inputs([2048], 4, 1, 128, "bf16", 23)
+    q = W.bits_to_f32(inp["q"]) * np.float32(0.25)
+    k = W.bits_to_f32(inp["k"]) * np.float32(0.25)
+    q[:, :, 127] = 8.0
+    k[:, 0, 127] = np.linspace(0.0, rise, 2048, dtype=np.float32)
+    inp["q"], inp["k"] = W.bf16_bits(q), W.bf16_bits(k)
+    check_prefill(inp, 512, 256, 1e4)
+
+
 def test_prefill_inputs_untouched_and_deterministic():
     torch = _torch()
     _say("prefill determinism")
