@@ -46,6 +46,7 @@ struct Params {
   float* part;  // [B][Hq][nsplit][slots][D + 2]  (O unnormalised, m (log2), l)
   const int32_t* seq_L;
   const float2* tab;
+  const _Float16* tab16;  // the same rows in half, (cos, cos, sin, sin) per frequency pair
   int B, Hq, Hkv, ratio, nsplit, kps, max_L;
   int wph;    // wavefronts per KV head in a workgroup (bf16 split kernel)
   int slots;  // partial states per (sequence, head, split)
@@ -101,6 +102,7 @@ struct SplitCtx {
   const uint16_t* kc;  // this (sequence, KV head)'s key rows
   const uint16_t* vc;
   const float2* tab;
+  const _Float16* tab16;
   const uint16_t* klane;     // kc + col*ss + g*8: this lane's K piece of block row 0
   const uint16_t* vlane[2];  // vc + (lane/CPR)*ss + swizzled chunk, for (t*RPI) % 8 = 0 / 4
   const f16x8* ql;     // LDS: query fragments rotated at qpos, [t][g][head]
@@ -173,25 +175,32 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     kpos = klocal ? (PR ? 0 : jk) : (PR ? jk - frem : frem);
   }
   const float ksgn = PR && !klocal ? -1.f : 1.f;
+  // rotation in packed half: the bf16 key converts to half exactly, the half
+  // cos/sin carry at most 2^-12 absolute error, and the result is rounded to
+  // half for the MFMA either way
   f16x8 a[NT];
-  const float4* cs4 = reinterpret_cast<const float4*>(c.tab + kpos * H + g * 8);
+  const uint4* cs8 = reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(kpos) * (H / 2) + g * 4) * 4);
+  const f16x2 sgn2 = {static_cast<_Float16>(ksgn), static_cast<_Float16>(ksgn)};
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
-    const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
+    const uint4 ca = cs8[t * 8], cb = cs8[t * 8 + 1];  // frequency pairs e2 = 0, 1 and 2, 3
+    const uint32_t cw[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
-      const float4 cs = cs4[t * 16 + e2];  // (cos, sin) of features t*32 + g*8 + 2*e2, + 1
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int e = e2 * 2 + hh;
-        const float cc = hh ? cs.z : cs.x;
-        const float sn = PR ? (hh ? cs.w : cs.y) * ksgn : (hh ? cs.w : cs.y);
-        const float x1 = bf16_bits_to_float(static_cast<uint16_t>(u1[e >> 1] >> (16 * (e & 1))));
-        const float x2 = bf16_bits_to_float(static_cast<uint16_t>(u2[e >> 1] >> (16 * (e & 1))));
-        a[t][e] = static_cast<_Float16>(x1 * cc - x2 * sn);
-        a[t + HT][e] = static_cast<_Float16>(x2 * cc + x1 * sn);
-      }
+      const f16x2 cc = __builtin_bit_cast(f16x2, cw[2 * e2]);
+      f16x2 sn = __builtin_bit_cast(f16x2, cw[2 * e2 + 1]);
+      if constexpr (PR) sn = sn * sgn2;
+      const uint32_t u1[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
+      const uint32_t u2[4] = {kr[t + HT].x, kr[t + HT].y, kr[t + HT].z, kr[t + HT].w};
+      const uint32_t w1 = u1[e2], w2 = u2[e2];
+      const f16x2 x1 = {static_cast<_Float16>(__uint_as_float(w1 << 16)), static_cast<_Float16>(__uint_as_float(w1 & 0xffff0000u))};
+      const f16x2 x2 = {static_cast<_Float16>(__uint_as_float(w2 << 16)), static_cast<_Float16>(__uint_as_float(w2 & 0xffff0000u))};
+      const f16x2 o1 = x1 * cc - x2 * sn;
+      const f16x2 o2 = x2 * cc + x1 * sn;
+      a[t][2 * e2] = o1[0];
+      a[t][2 * e2 + 1] = o1[1];
+      a[t + HT][2 * e2] = o2[0];
+      a[t + HT][2 * e2 + 1] = o2[1];
     }
   }
 
@@ -302,6 +311,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   c.kc = static_cast<const uint16_t*>(p.kc) + b * p.sb + hkv * p.sh;
   c.vc = static_cast<const uint16_t*>(p.vc) + b * p.sb + hkv * p.sh;
   c.tab = p.tab;
+  c.tab16 = p.tab16;
   c.ql = sQl[wid];
   c.vblk = sV[wid];
   c.ss = p.ss;
@@ -655,8 +665,9 @@ int decode_num_splits(int B, int max_L, int Hkv) {
 size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D) {
   const int ns = decode_num_splits(B, max_L, Hkv);
   const size_t tab = align_up(static_cast<size_t>(max_L) * (D / 2) * sizeof(float2), 256);
+  const size_t tab16 = align_up(static_cast<size_t>(max_L) * D * sizeof(_Float16), 256);
   const size_t part = static_cast<size_t>(B) * Hq * ns * kWaves * (D + 2) * sizeof(float);  // slots <= kWaves
-  return tab + align_up(part, 256);
+  return tab + tab16 + align_up(part, 256);
 }
 
 hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
@@ -664,6 +675,8 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   const int ns = decode_num_splits(c.B, c.max_L, c.Hkv);
   char* ws = static_cast<char*>(c.ws);
   const size_t tab = align_up(static_cast<size_t>(c.max_L) * (c.D / 2) * sizeof(float2), 256);
+  const size_t tab16 = align_up(static_cast<size_t>(c.max_L) * c.D * sizeof(_Float16), 256);
+  _Float16* t16 = reinterpret_cast<_Float16*>(ws + tab);
   Params p{};
   p.q = c.q;
   p.kc = c.kc;
@@ -671,9 +684,10 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.sb = c.sb;
   p.ss = c.ss;
   p.sh = c.sh;
-  p.part = reinterpret_cast<float*>(ws + tab);
+  p.part = reinterpret_cast<float*>(ws + tab + tab16);
   p.seq_L = c.seq_L;
   p.tab = reinterpret_cast<const float2*>(ws);
+  p.tab16 = t16;
   p.B = c.B;
   p.Hq = c.Hq;
   p.Hkv = c.Hkv;
@@ -694,9 +708,10 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   // rows a decode reads: remote positions (all below w_pretrained) and each
   // sequence's local window; a pre-rotated cache reads row 0 and the
   // correction rows j - f(j), which cover the whole range
-  hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s)
+  _Float16* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
+  hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s, t16w)
                           : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B,
-                                                   c.w0, c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s);
+                                                   c.w0, c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s, t16w);
   if (e != hipSuccess) return e;
   const int ratio = c.Hq / c.Hkv;
   if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);

@@ -20,11 +20,13 @@ namespace jl {
 //
 // With seq_L given (decode), only rows a decode can read are written: rows
 // below `remote_rows` (every remote position f(j) < w_pretrained) and each
-// sequence's local window [L_b - w0, L_b).
+// sequence's local window [L_b - w0, L_b).  With tab16 given, the same rows
+// are also written as half: entry kp of row p holds (cos, cos, sin, sin) of
+// frequencies 2kp and 2kp + 1, the operand order of a packed-half rotation.
 constexpr int kRun = 32;
 
-__global__ void rope_table_kernel(float2* __restrict__ tab, int npos, int half, double theta,
-                                  double neg2_over_d, const int32_t* __restrict__ seq_L, int B,
+__global__ void rope_table_kernel(float2* __restrict__ tab, _Float16* __restrict__ tab16, int npos, int half,
+                                  double theta, double neg2_over_d, const int32_t* __restrict__ seq_L, int B,
                                   int w0, int remote_rows) {
   const int k = threadIdx.x % half;
   const int run = blockIdx.x * (blockDim.x / half) + threadIdx.x / half;
@@ -47,25 +49,32 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, int npos, int half, 
   for (int p = p0; p < pend; ++p) {
     bool need = all || p < remote_rows;
     for (int b = 0; b < B && !need; ++b) need = p >= seq_L[b] - w0 && p < seq_L[b];
-    if (need) tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    if (need) {
+      tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
+      if (tab16) {
+        _Float16* e = tab16 + (static_cast<int64_t>(p) * (half / 2) + k / 2) * 4 + (k & 1);
+        e[0] = static_cast<_Float16>(c);
+        e[2] = static_cast<_Float16>(s);
+      }
+    }
     const double cn = c * c1 - s * s1;
     s = s * c1 + c * s1;
     c = cn;
   }
 }
 
-hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s) {
-  return launch_rope_table_rows(tab, npos, D, theta, nullptr, 0, 0, npos, s);
+hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s, _Float16* tab16) {
+  return launch_rope_table_rows(tab, npos, D, theta, nullptr, 0, 0, npos, s, tab16);
 }
 
 hipError_t launch_rope_table_rows(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B,
-                                  int w0, int remote_rows, hipStream_t s) {
+                                  int w0, int remote_rows, hipStream_t s, _Float16* tab16) {
   const int half = D / 2;
   if (npos <= 0) return hipSuccess;
   const int runs = (npos + kRun - 1) / kRun;
   const int per_block = 256 / half;
   hipLaunchKernelGGL(rope_table_kernel, dim3((runs + per_block - 1) / per_block), dim3(per_block * half), 0, s,
-                     tab, npos, half, theta, -2.0 / static_cast<double>(D), seq_L, B, w0, remote_rows);
+                     tab, tab16, npos, half, theta, -2.0 / static_cast<double>(D), seq_L, B, w0, remote_rows);
   return hipGetLastError();
 }
 
