@@ -96,6 +96,23 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
 #endif
 }
 
+// Maximum of v over the lanes l, l ^ 16 (v_permlane16_swap: rows of 16
+// lanes trade places) and over l, l ^ 32 (v_permlane32_swap), on the VALU.
+__device__ __forceinline__ float xrow16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Loop-invariant state of one wavefront of the bf16 split kernel.
 template <int D>
 struct SplitCtx {
@@ -114,7 +131,8 @@ struct SplitCtx {
 };
 
 // Running state: O block nb in lane (col, g) holds feature nb*16 + col of
-// heads g*4 + rr; m (log2 domain) and l of head `col`.
+// heads g*4 + rr; m (log2 domain) of head `col`, and the part of its l from
+// the keys of lane group g (summed over g after the last block).
 template <int D>
 struct SplitState {
   f32x4 o[D / 16];
@@ -217,23 +235,31 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     for (int t = 0; t < NT; ++t)
       sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], c.ql[(t * 4 + g) * NR + c.qcol], sl, 0, 0, 0);
   }
+  // one logit set per key: outside the window edge the other set was not
+  // formed and is zero
   float sv[4];
+  if (all_remote || all_local) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int j = j0 + g * 4 + rr;
-    float v = all_remote ? sr[rr] : all_local ? sl[rr] : (c.qpos - j < c.w0 ? sl[rr] : sr[rr]);
-    if (TAIL && j >= c.kend) v = -INFINITY;
-    sv[rr] = v;
+    for (int rr = 0; rr < 4; ++rr) sv[rr] = sr[rr] + sl[rr];
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sv[rr] = c.qpos - (j0 + g * 4 + rr) < c.w0 ? sl[rr] : sr[rr];
+  }
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      if (j0 + g * 4 + rr >= c.kend) sv[rr] = -INFINITY;
   }
 
   // ---- online softmax with a lazy maximum: m only moves when a score
   // exceeds it by more than 2^8 (so exp2(s - m) <= 256); O and l are
-  // rescaled then, on a wave-uniform branch
-  float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-  const bool grow = bmax > st.m + 8.f;
-  if (__any(grow)) {
+  // rescaled then, on a wave-uniform branch.  Each lane checks its own four
+  // scores; the head's maximum over the block (lanes col, col + 16, + 32,
+  // + 48) is formed only on that branch.
+  const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  if (__any(lmax > st.m + 8.f)) {
+    const float bmax = xrow32_max(xrow16_max(lmax));
+    const bool grow = bmax > st.m + 8.f;
     const float m_new = grow ? bmax : st.m;
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     st.l *= alpha;
@@ -250,10 +276,7 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   float pv[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) pv[rr] = __builtin_amdgcn_exp2f(sv[rr] - st.m);
-  float bsum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-  bsum += __shfl_xor(bsum, 16);
-  bsum += __shfl_xor(bsum, 32);
-  st.l += bsum;
+  st.l += (pv[0] + pv[1]) + (pv[2] + pv[3]);  // this lane's keys; the head's sum is formed at the end
   // P as a bf16 high part plus a bf16 low part: on exact bf16 V the product
   // keeps ~16 bits of P
   const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
@@ -409,6 +432,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     if (r0 >= G) { r0 -= G; ++q0; }
   }
   if (j0 < kend) split_block<D, NR, true, PR>(c, qrf, st, j0, q0, r0);
+
+  st.l = xrow_sum(st.l);
 
   // ---- this wavefront's partial state: O feature nb*16 + col of head
   // g*4 + rr in register rr; m and l of head hh in lane hh
