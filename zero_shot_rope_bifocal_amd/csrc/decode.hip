@@ -701,7 +701,7 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   char* ws = static_cast<char*>(c.ws);
   const size_t tab = align_up(static_cast<size_t>(c.max_L) * (c.D / 2) * sizeof(float2), 256);
   const size_t tab16 = align_up(static_cast<size_t>(c.max_L) * c.D * sizeof(_Float16), 256);
-  _Float16* t16 = reinterpret_cast<_Float16*>(ws + tab);
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(ws + tab);
   Params p{};
   p.q = c.q;
   p.kc = c.kc;
@@ -712,7 +712,7 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.part = reinterpret_cast<float*>(ws + tab + tab16);
   p.seq_L = c.seq_L;
   p.tab = reinterpret_cast<const float2*>(ws);
-  p.tab16 = t16;
+  p.tab16 = reinterpret_cast<const _Float16*>(t16);
   p.B = c.B;
   p.Hq = c.Hq;
   p.Hkv = c.Hkv;
@@ -733,7 +733,7 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   // rows a decode reads: remote positions (all below w_pretrained) and each
   // sequence's local window; a pre-rotated cache reads row 0 and the
   // correction rows j - f(j), which cover the whole range
-  _Float16* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
+  uint16_t* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
   hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s, t16w)
                           : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B,
                                                    c.w0, c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s, t16w);

@@ -25,7 +25,7 @@ namespace jl {
 // frequencies 2kp and 2kp + 1, the operand order of a packed-half rotation.
 constexpr int kRun = 32;
 
-__global__ void rope_table_kernel(float2* __restrict__ tab, _Float16* __restrict__ tab16, int npos, int half,
+__global__ void rope_table_kernel(float2* __restrict__ tab, uint16_t* __restrict__ tab16, int npos, int half,
                                   double theta, double neg2_over_d, const int32_t* __restrict__ seq_L, int B,
                                   int w0, int remote_rows) {
   const int k = threadIdx.x % half;
@@ -49,13 +49,16 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, _Float16* __restrict
   for (int p = p0; p < pend; ++p) {
     bool need = all || p < remote_rows;
     for (int b = 0; b < B && !need; ++b) need = p >= seq_L[b] - w0 && p < seq_L[b];
-    if (need) {
-      tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
-      if (tab16) {
-        _Float16* e = tab16 + (static_cast<int64_t>(p) * (half / 2) + k / 2) * 4 + (k & 1);
-        e[0] = static_cast<_Float16>(c);
-        e[2] = static_cast<_Float16>(s);
-      }
+    if (need) tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    if (tab16) {
+      // frequencies k and k + 1 sit in neighbouring lanes; the even lane
+      // writes the pair's 8-byte entry (every lane of the wave takes part in
+      // the exchange, so it stays outside the `need` branch)
+      const uint32_t cs = pack_f16x2(static_cast<float>(c), static_cast<float>(s));
+      const uint32_t odd = __shfl_down(cs, 1);
+      if (need && !(k & 1))
+        *reinterpret_cast<uint2*>(tab16 + (static_cast<int64_t>(p) * (half / 2) + k / 2) * 4) =
+            make_uint2((cs & 0xffffu) | (odd << 16), (cs >> 16) | (odd & 0xffff0000u));
     }
     const double cn = c * c1 - s * s1;
     s = s * c1 + c * s1;
@@ -63,12 +66,12 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, _Float16* __restrict
   }
 }
 
-hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s, _Float16* tab16) {
+hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s, uint16_t* tab16) {
   return launch_rope_table_rows(tab, npos, D, theta, nullptr, 0, 0, npos, s, tab16);
 }
 
 hipError_t launch_rope_table_rows(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B,
-                                  int w0, int remote_rows, hipStream_t s, _Float16* tab16) {
+                                  int w0, int remote_rows, hipStream_t s, uint16_t* tab16) {
   const int half = D / 2;
   if (npos <= 0) return hipSuccess;
   const int runs = (npos + kRun - 1) / kRun;
