@@ -367,3 +367,62 @@ def test_chunked_prefill_across_G_boundary_same_cache():
         el = float(np.max(np.abs(lse.cpu().numpy().T - l_ref)))
         _say(f"L={L} (G={jl.group_size(L, wp)}): max|dO|={eo:.3e} max|dLSE|={el:.3e}")
         assert eo <= TOL["bf16"] and el <= TOL["bf16"], (L, eo, el)
+
+
+# ---------------------------------------------------------------- sweeps
+
+def _random_prefill_configs(n, seed):
+    """Seeded small configurations: ragged lengths (some not multiples of 64,
+    some shorter than one tile), GQA ratios 1..8 including odd ones, head_dim
+    64 / 128, windows from 0 to beyond L and group sizes from 1 to ~8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(1, 1400, size=B)]
+        Hkv = int(rng.choice([1, 2, 3]))
+        ratio = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        d = int(rng.choice([64, 128]))
+        dt = "bf16" if i % 4 else "f32"
+        Lmax = max(lens)
+        wp = int(rng.integers(max(1, Lmax // 8), Lmax + 200))
+        w0 = int(rng.choice([0, 1, int(rng.integers(2, 400)), Lmax + 5]))
+        theta = float(rng.choice([1e4, 1e6]))
+        out.append((lens, Hkv * ratio, Hkv, d, dt, wp, w0, theta, 100 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_prefill_configs(12, 2024), ids=[f"r{i}" for i in range(12)])
+def test_prefill_random_configs(case):
+    _torch()
+    lens, Hq, Hkv, d, dt, wp, w0, theta, seed = case
+    _say("random prefill", case)
+    inp = W.prefill_inputs(lens, Hq, Hkv, d, dt, seed)
+    check_prefill(inp, wp, w0, theta)
+
+
+def _random_decode_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 5))
+        S = int(rng.integers(16, 3000))
+        seq_L = [int(x) for x in rng.integers(1, S + 1, size=B)]
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        ratio = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        d = int(rng.choice([64, 128]))
+        dt = "bf16" if i % 4 else "f32"
+        wp = int(rng.integers(max(1, S // 8), S + 200))
+        w0 = int(rng.choice([0, 1, int(rng.integers(2, 600)), S + 5]))
+        theta = float(rng.choice([1e4, 1e6]))
+        out.append((B, S, seq_L, Hkv * ratio, Hkv, d, dt, wp, w0, theta, 200 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_decode_configs(12, 2025), ids=[f"r{i}" for i in range(12)])
+def test_decode_random_configs(case):
+    _torch()
+    B, S, seq_L, Hq, Hkv, d, dt, wp, w0, theta, seed = case
+    _say("random decode", case)
+    inp = W.decode_inputs(B, S, Hq, Hkv, d, dt, seed, seq_L=seq_L)
+    check_decode(inp, wp, w0, theta)
