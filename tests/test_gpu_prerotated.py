@@ -54,6 +54,29 @@ PREFILL_CASES = [
 ]
 
 
+
+
+def _random_prefill_cases(n, seed):
+    """Seeded extra cases: ragged lengths, optional query chunks, GQA ratios
+    1..8, d 64 / 128, windows from 0 to beyond L."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        lens = [int(x) for x in rng.integers(2, 1300, size=B)]
+        q_lens = None if i % 2 else [int(rng.integers(1, L + 1)) for L in lens]
+        Hkv = int(rng.choice([1, 2]))
+        ratio = int(rng.choice([1, 2, 3, 4, 8]))
+        Lmax = max(lens)
+        out.append((lens, q_lens, Hkv * ratio, Hkv, int(rng.choice([64, 128])), "bf16" if i % 3 else "f32",
+                    int(rng.integers(max(1, Lmax // 6), Lmax + 100)), int(rng.choice([0, 1, int(rng.integers(2, 300)), Lmax + 3])),
+                    float(rng.choice([1e4, 1e6])), 300 + i))
+    return out
+
+
+PREFILL_CASES += _random_prefill_cases(6, 2026)
+
+
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"case{i}" for i in range(len(PREFILL_CASES))])
 def test_prefill_prerotated(case):
     torch = _torch()
@@ -95,6 +118,25 @@ DECODE_CASES = [
     (3, 800, [800, 65, 5], 8, 2, 128, "f32", 100, 50, 1e4, 73),
     (7, 1024, [255, 256, 257, 512, 513, 768, 769], 8, 2, 128, "bf16", 256, 64, 1e4, 75),  # G 1..4
 ]
+
+
+
+
+def _random_decode_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(8, 2500))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        ratio = int(rng.choice([1, 2, 4, 6, 8]))
+        out.append((B, S, [int(x) for x in rng.integers(1, S + 1, size=B)], Hkv * ratio, Hkv, int(rng.choice([64, 128])),
+                    "bf16" if i % 3 else "f32", int(rng.integers(max(1, S // 6), S + 100)),
+                    int(rng.choice([0, 1, int(rng.integers(2, 500)), S + 3])), float(rng.choice([1e4, 1e6])), 400 + i))
+    return out
+
+
+DECODE_CASES += _random_decode_cases(6, 2027)
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[f"case{i}" for i in range(len(DECODE_CASES))])
