@@ -6,6 +6,7 @@ seeded random rows; all heads).  Decode is checked in full.
 Tolerance: max abs error 2e-2 on O and LSE (bf16 outputs).
 """
 import concurrent.futures as cf
+import os
 
 import numpy as np
 import pytest
@@ -27,6 +28,10 @@ def _torch():
 
 def _say(*a):
     print("[case]", *a, flush=True)
+    log = os.environ.get("JL_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            print(os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], *a, file=f)
 
 
 def oracle_rows_parallel(q_rows, k, v, rows, L, wp, w0, theta, Hq, Hkv):
