@@ -21,7 +21,7 @@ softmax, no merge):
 * Full local and remote logit rows, mask-select by distance, causal softmax,
   times V.
 
-Readings where the pages are silent (each is listed in the design doc as well):
+Readings where the pages are silent:
 * RoPE itself is not defined on the pages: standard RoPE with
   theta_k = theta^(-2k/d), rotate-half pairing (dims k and k + d/2).
 * The remote branch rotates each token by f of its own absolute position, with
