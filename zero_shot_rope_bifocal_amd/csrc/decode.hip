@@ -736,7 +736,7 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   uint16_t* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
   hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s, t16w)
                           : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B,
-                                                   c.w0, c.w_pretrained < c.max_L ? c.w_pretrained : c.max_L, s, t16w);
+                                                   c.w0, c.w_pretrained, s, t16w);
   if (e != hipSuccess) return e;
   const int ratio = c.Hq / c.Hkv;
   if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);

@@ -53,10 +53,13 @@ void prefill_bf16_tile_shape(int ratio, int* BM, int* BN);
 // tab16 (optional): the same rows in half, entry kp of a row = (cos, cos,
 // sin, sin) of frequencies 2kp and 2kp + 1.
 hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s, uint16_t* tab16 = nullptr);
-// Same table, writing only the rows below remote_rows and each sequence's
-// window [seq_L[b] - w0, seq_L[b]) (the rows a decode reads).
+// Same table, writing only the rows a decode reads: those below
+// min(w_pretrained, npos) (every remote position), each sequence's window
+// [seq_L[b] - w0, seq_L[b]) and its query rows.  With tab16 given the fp32
+// rows are written for the query rows alone (the bf16 split kernel rotates
+// keys from the half rows).
 hipError_t launch_rope_table_rows(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B,
-                                  int w0, int remote_rows, hipStream_t s, uint16_t* tab16 = nullptr);
+                                  int w0, int w_pretrained, hipStream_t s, uint16_t* tab16 = nullptr);
 // Prefill in two stages on one workspace: prepare (cos/sin table; for bf16
 // also the rotated key copies and transposed values) and attend.
 hipError_t launch_prefill_bf16_prepare(const PrefillCall& c, hipStream_t s);

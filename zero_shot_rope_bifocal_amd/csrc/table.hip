@@ -18,45 +18,69 @@ namespace jl {
 // table thus keeps full fp32 accuracy at positions near 2^17, where an fp32
 // angle would be off by ~1e-2 rad.
 //
-// With seq_L given (decode), only rows a decode can read are written: rows
-// below `remote_rows` (every remote position f(j) < w_pretrained) and each
-// sequence's local window [L_b - w0, L_b).  With tab16 given, the same rows
-// are also written as half: entry kp of row p holds (cos, cos, sin, sin) of
-// frequencies 2kp and 2kp + 1, the operand order of a packed-half rotation.
+// With seq_L given (decode), only rows a decode can read are written.  Work
+// items (one run of kRun rows for one frequency; a wavefront holds whole
+// runs): items [0, n0) cover the rows below `rows0` (every remote position
+// f(j) < w_pretrained); items n0 + b * nw + r run r of sequence b's local
+// window [max(L_b - w0, rows0), L_b), skipped when sequence b - 1 has the
+// same length; items n0 + B * nw + b the two rows its query is rotated with,
+// L_b - 1 and f(L_b - 1).  With q32_only set (the bf16 decode, whose keys
+// read the half rows only) the fp32 rows are written for the query rows
+// alone.  With tab16 given, the same rows are also written as half: entry kp
+// of row p holds (cos, cos, sin, sin) of frequencies 2kp and 2kp + 1, the
+// operand order of a packed-half rotation.  Runs start at multiples of kRun,
+// so a row that two items write (overlapping windows) gets the same bits.
 constexpr int kRun = 32;
 
 __global__ void rope_table_kernel(float2* __restrict__ tab, uint16_t* __restrict__ tab16, int npos, int half,
                                   double theta, double neg2_over_d, const int32_t* __restrict__ seq_L, int B,
-                                  int w0, int remote_rows) {
+                                  int w0, int rows0, int nw, int w_pretrained, int q32_only) {
   const int k = threadIdx.x % half;
-  const int run = blockIdx.x * (blockDim.x / half) + threadIdx.x / half;
-  const int p0 = run * kRun;
-  if (p0 >= npos) return;
-  const int pend = min(npos, p0 + kRun);
-  bool all = seq_L == nullptr || pend <= remote_rows;
-  if (!all) {
-    bool any = p0 < remote_rows;
-    for (int b = 0; b < B && !any; ++b) {
-      const int Lb = seq_L[b];
-      any = Lb - w0 < pend && Lb > p0;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * (blockDim.x / half) + threadIdx.x / half;
+  const int n0 = (rows0 + kRun - 1) / kRun;
+  int p0 = 0, hi = rows0;
+  if (item < n0) {
+    p0 = static_cast<int>(item) * kRun;
+  } else {
+    if (!seq_L) return;
+    const int64_t wi = item - n0;
+    const int b = static_cast<int>(wi < static_cast<int64_t>(B) * nw ? wi / nw : wi - static_cast<int64_t>(B) * nw);
+    if (b >= B) return;
+    const int Lb = seq_L[b];
+    if (Lb < 1 || Lb > npos) return;  // a sequence the decode leaves unwritten
+    if (wi >= static_cast<int64_t>(B) * nw) {
+      // the query's rows, fp32 only; without q32_only the other items hold
+      // them, except row L_b - 1 when the window is empty
+      const double inv = pow(theta, neg2_over_d * k);
+      const int rows[2] = {Lb - 1, (Lb - 1) / group_size(Lb, w_pretrained)};
+      for (int i = 0; i < 2; ++i) {
+        if (!q32_only && (rows[i] < rows0 || w0 > 0)) continue;
+        double sv, cv;
+        sincos(static_cast<double>(rows[i]) * inv, &sv, &cv);
+        tab[static_cast<int64_t>(rows[i]) * half + k] = make_float2(static_cast<float>(cv), static_cast<float>(sv));
+      }
+      return;
     }
-    if (!any) return;
+    if (b > 0 && seq_L[b - 1] == Lb) return;
+    const int lo = max(Lb - w0, rows0);
+    hi = Lb;
+    if (lo >= hi) return;
+    p0 = lo / kRun * kRun + static_cast<int>(wi % nw) * kRun;
   }
+  if (p0 >= hi) return;
+  const int pend = min(hi, p0 + kRun);
   const double inv = pow(theta, neg2_over_d * k);
   double s, c, s1, c1;
   sincos(static_cast<double>(p0) * inv, &s, &c);
   sincos(inv, &s1, &c1);
   for (int p = p0; p < pend; ++p) {
-    bool need = all || p < remote_rows;
-    for (int b = 0; b < B && !need; ++b) need = p >= seq_L[b] - w0 && p < seq_L[b];
-    if (need) tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    if (!q32_only) tab[static_cast<int64_t>(p) * half + k] = make_float2(static_cast<float>(c), static_cast<float>(s));
     if (tab16) {
-      // frequencies k and k + 1 sit in neighbouring lanes; the even lane
-      // writes the pair's 8-byte entry (every lane of the wave takes part in
-      // the exchange, so it stays outside the `need` branch)
+      // frequencies k and k + 1 sit in neighbouring lanes of one run; the
+      // even lane writes the pair's 8-byte entry
       const uint32_t cs = pack_f16x2(static_cast<float>(c), static_cast<float>(s));
       const uint32_t odd = __shfl_down(cs, 1);
-      if (need && !(k & 1))
+      if (!(k & 1))
         *reinterpret_cast<uint2*>(tab16 + (static_cast<int64_t>(p) * (half / 2) + k / 2) * 4) =
             make_uint2((cs & 0xffffu) | (odd << 16), (cs >> 16) | (odd & 0xffff0000u));
     }
@@ -66,19 +90,35 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, uint16_t* __restrict
   }
 }
 
+namespace {
+hipError_t launch_table(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B, int w0, int rows0,
+                        int w_pretrained, hipStream_t s, uint16_t* tab16) {
+  const int half = D / 2;
+  const int per_block = 256 / half;
+  const int n0 = (rows0 + kRun - 1) / kRun;
+  // runs of one window from its aligned start
+  const int nw = seq_L ? ((w0 < npos ? w0 : npos) + kRun - 1) / kRun + 1 : 0;
+  const int64_t items = n0 + (static_cast<int64_t>(nw) + 1) * (seq_L ? B : 0);
+  const int64_t blocks = (items + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(per_block * half), 0, s, tab, tab16,
+                     npos, half, theta, -2.0 / static_cast<double>(D), seq_L, B, w0, rows0, nw, w_pretrained,
+                     seq_L && tab16 ? 1 : 0);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_rope_table(float2* tab, int npos, int D, double theta, hipStream_t s, uint16_t* tab16) {
-  return launch_rope_table_rows(tab, npos, D, theta, nullptr, 0, 0, npos, s, tab16);
+  if (npos <= 0) return hipSuccess;
+  return launch_table(tab, npos, D, theta, nullptr, 0, 0, npos, 1, s, tab16);
 }
 
 hipError_t launch_rope_table_rows(float2* tab, int npos, int D, double theta, const int32_t* seq_L, int B,
-                                  int w0, int remote_rows, hipStream_t s, uint16_t* tab16) {
-  const int half = D / 2;
-  if (npos <= 0) return hipSuccess;
-  const int runs = (npos + kRun - 1) / kRun;
-  const int per_block = 256 / half;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((runs + per_block - 1) / per_block), dim3(per_block * half), 0, s,
-                     tab, tab16, npos, half, theta, -2.0 / static_cast<double>(D), seq_L, B, w0, remote_rows);
-  return hipGetLastError();
+                                  int w0, int w_pretrained, hipStream_t s, uint16_t* tab16) {
+  if (npos <= 0 || B <= 0) return hipSuccess;
+  return launch_table(tab, npos, D, theta, seq_L, B, w0, w_pretrained < npos ? w_pretrained : npos, w_pretrained, s,
+                      tab16);
 }
 
 // Query positions, remote positions and per-sequence G of a packed batch:
