@@ -256,6 +256,29 @@ def test_decode_matches_oracle(case):
     check_decode(inp, wp, w0, theta)
 
 
+# Decode cases aimed at which cos/sin rows the decode writes: neighbours of
+# equal length (their window is written once), overlapping windows that start
+# off the 32-row run grid, a sequence shorter than w_pretrained, and empty
+# windows (w0 = 0, where the query's own row is written on its own); d 128
+# (one run per wavefront) and d 64 (two runs per wavefront), both dtypes.
+TABLE_ROW_CASES = [
+    # (B, S, seq_L, Hq, Hkv, d, dtype, wp, w0, theta, seed)
+    (6, 2400, [2400, 2400, 2333, 2301, 2400, 90], 16, 4, 128, "bf16", 600, 250, 1e4, 41),
+    (6, 2400, [2400, 2400, 2333, 2301, 2400, 90], 16, 4, 128, "f32", 600, 250, 1e4, 42),
+    (4, 1300, [1300, 1300, 1299, 7], 8, 2, 64, "bf16", 256, 0, 1e4, 43),
+    (4, 1300, [1300, 1300, 1299, 7], 8, 2, 64, "f32", 256, 0, 1e4, 44),
+]
+
+
+@pytest.mark.parametrize("case", TABLE_ROW_CASES, ids=[f"rows{i}" for i in range(len(TABLE_ROW_CASES))])
+def test_decode_table_rows(case):
+    _torch()
+    B, S, seq_L, Hq, Hkv, d, dt, wp, w0, theta, seed = case
+    _say("decode table rows", case)
+    inp = W.decode_inputs(B, S, Hq, Hkv, d, dt, seed, seq_L=seq_L)
+    check_decode(inp, wp, w0, theta)
+
+
 def test_decode_strided_cache_and_untouched():
     """A cache laid out [S, B, Hkv, d] (non-default strides) is read in place
     and left byte-identical."""
