@@ -203,6 +203,8 @@ size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int
  *   o   device [B, Hq, head_dim] dtype output; lse device [B, Hq] float or NULL
  *   seq_L device int32 [B]: keys valid in sequence b, the new token included
  *       (1 <= seq_L[b] <= max_L); the query sits at position seq_L[b]-1.
+ *       A sequence outside that range (the lengths live on the device and
+ *       are not checked on the host) is left unwritten in o and lse.
  *   workspace: device, >= jl_bifocal_decode_workspace_size(...) bytes.
  */
 int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -279,6 +279,37 @@ def test_decode_table_rows(case):
     check_decode(inp, wp, w0, theta)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_invalid_lengths_left_unwritten(dt):
+    """A sequence whose length breaks 1 <= L <= max_L is skipped by every
+    decode kernel (its o and lse keep what the caller stored there); the
+    other sequences of the batch match the oracle."""
+    torch = _torch()
+    B, S, Hq, Hkv, d, wp, w0, theta = 4, 600, 8, 2, 128, 256, 100, 1e4
+    good = [600, 600, 300, 17]
+    inp = W.decode_inputs(B, S, Hq, Hkv, d, dt, 45, seq_L=good)
+    q = W.to_device(inp["q"], dt)
+    k = W.to_device(inp["k"], dt)
+    v = W.to_device(inp["v"], dt)
+    lens = np.array([600, 0, 300, 601], dtype=np.int32)  # sequence 1: L = 0; sequence 3: L > max_L
+    _say("decode invalid lengths", dt, lens.tolist())
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((B, Hq), 5.0, dtype=torch.float32, device=q.device)
+    jl.decode(q, k, v, torch.from_numpy(lens).cuda(), wp, w0, theta, max_L=S, out=out, lse=lse, return_lse=True)
+    torch.cuda.synchronize()
+    o_gpu = out.float().cpu().numpy().astype(np.float64)
+    l_gpu = lse.cpu().numpy().astype(np.float64)
+    for b in (1, 3):
+        assert np.all(o_gpu[b] == 7.0) and np.all(l_gpu[b] == 5.0), b
+    o_ref, l_ref = oracle.bifocal_decode(W.as_f64(inp["q"], dt), W.as_f64(inp["k"], dt), W.as_f64(inp["v"], dt),
+                                         inp["seq_L"], wp, w0, theta)
+    for b in (0, 2):
+        err_o = np.max(np.abs(o_gpu[b] - o_ref[b]))
+        err_l = np.max(np.abs(l_gpu[b] - l_ref[b]))
+        _say(f"seq {b}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+        assert err_o <= TOL[dt] and err_l <= TOL[dt], (b, err_o, err_l)
+
+
 def test_decode_strided_cache_and_untouched():
     """A cache laid out [S, B, Hkv, d] (non-default strides) is read in place
     and left byte-identical."""

@@ -597,13 +597,16 @@ __global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
 // over the partials (coalesced reads).
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nparts, void* o,
-                                                    float* lse, int bf16) {
+                                                    float* lse, int bf16, const int32_t* __restrict__ seq_L,
+                                                    int Hq, int max_L) {
   constexpr int kMaxParts = 1024;
   __shared__ float sw[kMaxParts];
   __shared__ float sred[D / 64];
   __shared__ float sM, sden;
   const int bh = blockIdx.x;  // b * Hq + h
   const int t = threadIdx.x;
+  const int L = seq_L[bh / Hq];
+  if (L < 1 || L > max_L) return;  // outside the documented contract: left unwritten, as in the split kernel
   const float* pp = part + static_cast<int64_t>(bh) * nparts * (D + 2);
   float mx = -INFINITY;
   for (int s = t; s < nparts; s += D) mx = fmaxf(mx, pp[s * (D + 2) + D]);
@@ -745,9 +748,11 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int nparts = ns * p.slots;
   if (c.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(128), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(128), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0,
+                       c.seq_L, c.Hq, c.max_L);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0);
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0,
+                       c.seq_L, c.Hq, c.max_L);
   return hipGetLastError();
 }
 
