@@ -92,7 +92,11 @@ size_t jl_bifocal_prefill_workspace_size(int dtype, int B, int total_k, int max_
  *       0 .. L_b-1 and its Lq_b queries sit at the last Lq_b positions
  *       (L_b - Lq_b .. L_b - 1; a chunk of a longer prefill); Lq_b <= L_b is
  *       required.  G_b is computed from L_b on the device.
- *   max_seqlen_q / max_seqlen_k: upper bounds of Lq_b / L_b.
+ *   max_seqlen_q / max_seqlen_k: upper bounds of Lq_b / L_b.  A sequence
+ *       that breaks Lq_b <= L_b, Lq_b <= max_seqlen_q or L_b <= max_seqlen_k
+ *       (lengths live on the device and are not checked on the host) is left
+ *       unwritten in o and lse; the inclusion-exclusion route leaves its rows
+ *       unspecified.
  *   w_pretrained >= 1, w0 >= 0, rope_theta > 0.
  *   softmax_scale: 0 selects 1/sqrt(head_dim).
  *   workspace: device, >= jl_bifocal_prefill_workspace_size(...) bytes,

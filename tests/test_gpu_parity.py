@@ -163,6 +163,38 @@ def test_chunked_prefill_matches_oracle(dt):
     check_prefill(inp, 256, 100, 1e4)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_contract_breaks_left_unwritten(dt):
+    """Sequences whose lengths exceed the bounds passed (Lq > max_seqlen_q,
+    L > max_seqlen_k) are skipped: their rows of o and lse keep what the
+    caller stored; the valid sequence matches the oracle."""
+    torch = _torch()
+    wp, w0, theta = 128, 60, 1e4
+    inp = W.prefill_inputs([300, 250, 400], 8, 2, 128, dt, 46, q_lens=[100, 200, 50])
+    _say("prefill contract breaks", dt)
+    q = W.to_device(inp["q"], dt)
+    k = W.to_device(inp["k"], dt)
+    v = W.to_device(inp["v"], dt)
+    cu_q = torch.from_numpy(inp["cu_q"]).cuda()
+    cu_k = torch.from_numpy(inp["cu_k"]).cuda()
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((8, q.shape[0]), 5.0, dtype=torch.float32, device=q.device)
+    # sequence 1: Lq = 200 > max_seqlen_q = 150; sequence 2: L = 400 > max_seqlen_k = 300
+    jl.prefill(q, k, v, cu_q, 150, wp, w0, theta, cu_seqlens_k=cu_k, max_seqlen_k=300, out=out, lse=lse,
+               return_lse=True)
+    torch.cuda.synchronize()
+    o_gpu = out.float().cpu().numpy().astype(np.float64)
+    l_gpu = lse.cpu().numpy().astype(np.float64)
+    assert np.all(o_gpu[100:] == 7.0) and np.all(l_gpu[:, 100:] == 5.0)
+    qq = W.as_f64(inp["q"][:100], dt)
+    o_ref, l_ref = oracle.bifocal_sequence(qq, W.as_f64(inp["k"][:300], dt), W.as_f64(inp["v"][:300], dt),
+                                           np.arange(200, 300), 300, wp, w0, theta)
+    err_o = np.max(np.abs(o_gpu[:100] - o_ref))
+    err_l = np.max(np.abs(l_gpu[:, :100].T - l_ref))
+    _say(f"seq 0: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+    assert err_o <= TOL[dt] and err_l <= TOL[dt], (err_o, err_l)
+
+
 def test_prefill_peaked_keys():
     _torch()
     _say("peaked keys")
