@@ -14,8 +14,10 @@ whole prefill call (algorithmic FLOPs = 4 * d * Hq * L(L+1)/2: one logit and
 one PV product per causal pair).  The decode rate (algorithmic bytes = K and
 V read once plus Q and O) is reported beside it.  `roofline` covers the
 dominant kernel (the prefill attention kernel) timed by itself with HIP
-events on the stream it runs on; `cpu_baseline` times the fp64 oracle on a
-bounded sample of query rows of the same workload.
+events on the stream it runs on; `cpu_baseline` times the fp64 oracle on the
+host cores (one worker process per core) on a bounded sample of the same
+workloads: random query-row blocks of the prefill, whole sequences of the
+decode.
 """
 from __future__ import annotations
 
@@ -64,32 +66,84 @@ def load_traffic(kernel: str, digest: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, w, budget_s: float):
-    """Times the oracle, as it stands, on query rows of the 128K workload
-    until the time budget is spent.  Returns (TFLOP/s, rows, seconds,
-    threads)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(kind: str, name: str, wid: int, nworkers: int, budget_s: float):
+    """One CPU-baseline worker (a spawned process with one BLAS thread): draws
+    its own share of the workload's inputs (untimed), then runs the oracle, as
+    it stands, on its units until the budget is spent.  Returns (work, oracle
+    seconds, units) with work in FLOP (prefill) or algorithmic bytes (decode)."""
     import numpy as np
     import oracle
     from zero_shot_rope_bifocal_amd import workloads as W
+    w = W.WORKLOADS[name]
+    t_end = time.perf_counter() + budget_s
+    work = secs = 0.0
+    units = 0
+    if kind == "prefill":
+        L, Hq, Hkv, d = w["lens"][0], w["Hq"], w["Hkv"], w["d"]
+        r = Hq // Hkv
+        kb, vb = W.prefill_kv(name)
+        h = wid % Hkv  # this worker's KV head and its query heads
+        k = W.as_f64(kb[:, h:h + 1], "bf16")
+        v = W.as_f64(vb[:, h:h + 1], "bf16")
+        del kb, vb
+        rng = np.random.default_rng(1000 + wid)
+        while time.perf_counter() < t_end:
+            row0 = int(rng.integers(0, L - 8))
+            q = W.as_f64(W.prefill_q_rows(name, row0, 8)[:, h * r:(h + 1) * r], "bf16")
+            rows = np.arange(row0, row0 + 8)
+            t0 = time.perf_counter()
+            oracle.bifocal_sequence(q, k, v, rows, L, w["w_pretrained"], w["w0"], w["theta"])
+            secs += time.perf_counter() - t0
+            work += float(sum(4.0 * d * r * (i + 1) for i in rows))
+            units += 1
+    else:
+        for b in range(wid, w["B"], nworkers):
+            if time.perf_counter() >= t_end:
+                break
+            qb, kb, vb = W.decode_sequence(name, b)
+            q, k, v = (W.as_f64(x, "bf16") for x in (qb, kb, vb))
+            del qb, kb, vb
+            t0 = time.perf_counter()
+            oracle.bifocal_decode(q, k, v, np.array([w["L"]], np.int32), w["w_pretrained"], w["w0"], w["theta"])
+            secs += time.perf_counter() - t0
+            work += float(w["L"] * w["Hkv"] * w["d"] * 2 * 2 + 2 * w["Hq"] * w["d"] * 2)
+            units += 1
+    return work, secs, units
+
+
+def cpu_baseline(kind: str, name: str, budget_s: float, workers: int):
+    """The oracle on all host cores: `workers` spawned processes, one BLAS
+    thread each, every one timing its own oracle calls on its share of the
+    workload.  They run side by side, so the throughput is the sum of the
+    per-worker rates.  Returns (rate, work done, units, workers)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"  # inherited by the spawned workers only (this process's BLAS is set up)
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    L = w["lens"][0]
-    k = W.as_f64(inp["k"], "bf16")
-    v = W.as_f64(inp["v"], "bf16")
-    rng = np.random.default_rng(99)
-    order = rng.permutation(L)
-    done, flops, t0 = 0, 0.0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < L:
-        rows = np.sort(order[done:done + 8])
-        q = W.as_f64(inp["q"][rows], "bf16")
-        oracle.bifocal_sequence(q, k, v, rows, L, w["w_pretrained"], w["w0"], w["theta"])
-        flops += sum(4.0 * w["d"] * w["Hq"] * (int(i) + 1) for i in rows)
-        done += len(rows)
-    dt = time.perf_counter() - t0
-    return flops / dt / 1e12, done, dt, threads
+        with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+            res = list(ex.map(_oracle_worker, [kind] * workers, [name] * workers, range(workers),
+                              [workers] * workers, [budget_s] * workers))
+    finally:
+        for k, val in env.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    rate = sum(wk / sc for wk, sc, _ in res if sc > 0)
+    return rate, sum(r[0] for r in res), sum(r[2] for r in res), workers
 
 
 def main():
@@ -99,6 +153,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes for the CPU baseline (capped by os.cpu_count())")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one stage only (for profiling); the JSON line then covers that stage")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -130,7 +186,6 @@ def main():
     do_decode = args.only in (None, "decode")
     L = wp_["lens"][0]
     Hq, Hkv, d = wp_["Hq"], wp_["Hkv"], wp_["d"]
-    pin = None
     if do_prefill:
         log("generating 128K prefill inputs")
         pin = W.workload_inputs("long_bf16")
@@ -138,6 +193,7 @@ def main():
         k = W.to_device(pin["k"], "bf16", dev)
         v = W.to_device(pin["v"], "bf16", dev)
         cu = torch.from_numpy(pin["cu_q"]).to(dev)
+        del pin
         o = torch.empty_like(q)
         ws = torch.empty(jl.prefill_workspace_size(jl.JL_BF16, 1, L, L, Hq, Hkv, d), dtype=torch.uint8, device=dev)
     if do_decode:
@@ -150,6 +206,11 @@ def main():
         do = torch.empty_like(dq)
         dws = torch.empty(jl.decode_workspace_size(jl.JL_BF16, wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"]),
                           dtype=torch.uint8, device=dev)
+        # the cos/sin table of every position the caches hold: built once,
+        # like a model's RoPE cache, and read by every decode step
+        dtab = jl.rope_table(wd["L"], wd["d"], wd["theta"], device=dev)
+        dpart = torch.empty(jl.decode_with_table_workspace_size(jl.JL_BF16, wd["B"], wd["L"], wd["Hq"], wd["Hkv"],
+                                                                wd["d"]), dtype=torch.uint8, device=dev)
         del din
     if args.copy_mib:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
@@ -172,7 +233,8 @@ def main():
         if ev:
             ev[2].record()
         if do_decode:
-            jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
+            jl.decode_with_table(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], dtab, wd["L"], out=do,
+                                 workspace=dpart)
         if ev:
             ev[3].record()
 
@@ -227,7 +289,8 @@ def main():
             return a.elapsed_time(b) / reps
 
         plain = {"definition": "prefill: same kernels with w_pretrained = L (G = 1) and w0 = 0; decode: "
-                               "pre-rotated cache, w0 >= L (every key used as stored)"}
+                               "pre-rotated cache with w0 >= L, i.e. plain RoPE decode over a RoPE cache (no "
+                               "table, no key rotation, stored keys on the bf16 MFMA)"}
         if do_prefill:
             jl.prefill_prepare(k, v, cu, L, L, wp_["theta"], Hq=Hq, workspace=ws)
             p_ms = clock(lambda: jl.prefill_attend(q, k, v, cu, L, L, 0, wp_["theta"], ws, out=o))
@@ -235,10 +298,13 @@ def main():
             plain["prefill_attend_TFLOPs"] = round(fl / (p_ms * 1e-3) / 1e12, 2)
             plain["bifocal_over_plain_prefill_speed"] = round(p_ms / attn_ms, 4)
         if do_decode:
-            d_ms = clock(lambda: jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["L"] + 1, wd["theta"], out=do,
-                                           workspace=dws, prerotated=True), reps=5)
+            d_ms = clock(lambda: jl.decode_with_table(dq, dk, dv, seq, wd["w_pretrained"], wd["L"] + 1, dtab, wd["L"],
+                                                      out=do, workspace=dpart, prerotated=True), reps=20)
+            b_ms = clock(lambda: jl.decode_with_table(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], dtab, wd["L"],
+                                                      out=do, workspace=dpart), reps=20)
             plain["decode_ms"] = round(d_ms, 4)
-            plain["bifocal_decode_overhead"] = round(dec_ms / d_ms - 1.0, 4)
+            plain["bifocal_decode_ms_same_clock"] = round(b_ms, 4)
+            plain["bifocal_decode_overhead"] = round(b_ms / d_ms - 1.0, 4)
 
     # the pages' own route to the same prefill (three passes + LSE merge), on
     # the same inputs, after the timed region
@@ -265,25 +331,45 @@ def main():
               "routed_over_ie_speed": round(ie_ms / (prep_ms + attn_ms), 4)}
         del iws
 
-    # decode alone, 50 back-to-back calls after the timed region (median, min)
-    dec50 = None
+    # decode alone, 50 back-to-back calls after the timed region (median,
+    # min): over the prepared table, and building its cos/sin rows per call
+    dec50 = dec50_rows = None
     if do_decode and not args.only:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-        for a, b in ev:
-            a.record()
-            jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do, workspace=dws)
-            b.record()
-        torch.cuda.synchronize()
-        d50 = [a.elapsed_time(b) for a, b in ev]
-        dec50 = [round(median(d50), 4), round(min(d50), 4)]
+        def fifty(fn):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            d50 = [a.elapsed_time(b) for a, b in ev]
+            return [round(median(d50), 4), round(min(d50), 4)]
+        dec50 = fifty(lambda: jl.decode_with_table(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], dtab, wd["L"],
+                                                   out=do, workspace=dpart))
+        dec50_rows = fifty(lambda: jl.decode(dq, dk, dv, seq, wd["w_pretrained"], wd["w0"], wd["theta"], out=do,
+                                             workspace=dws))
 
     cpu = None
-    if not args.no_cpu_baseline and do_prefill:
-        log(f"cpu baseline ({args.cpu_seconds:.0f} s budget)")
-        val, rows, secs, threads = cpu_baseline(pin, wp_, args.cpu_seconds)
-        cpu = {"value": val, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"{rows} random query rows x {Hq} heads of the L=131072 prefill against all "
-                         f"keys, fp64 numpy, {secs:.1f} s"}
+    if not args.no_cpu_baseline:
+        # the machine's CPU share for one GPU is 16 cores, whatever os.cpu_count() says
+        workers = max(1, min(os.cpu_count() or 1, args.cpu_workers))
+        cpu = {"kind": "oracle", "cores": workers, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+               "threads_per_core": 1}
+        if do_prefill:
+            log(f"cpu baseline, prefill ({workers} workers, {args.cpu_seconds:.0f} s)")
+            val, fl, units, _ = cpu_baseline("prefill", "long_bf16", args.cpu_seconds, workers)
+            cpu.update(value=val / 1e12, unit="TFLOP/s",
+                       sample=f"{units} blocks of 8 consecutive query rows (random starts) x the 4 query heads of "
+                              f"one KV head, of the L=131072 prefill against all keys; fp64 numpy oracle; "
+                              f"{fl:.3g} FLOP in all")
+        if do_decode:
+            log(f"cpu baseline, decode ({workers} workers)")
+            val, by, units, _ = cpu_baseline("decode", "decode_bf16", max(args.cpu_seconds, 60.0), workers)
+            cpu["decode"] = {"value": val / 1e9, "unit": "GB/s", "sample":
+                             f"{units} of the 16 sequences of the 16 x 131072 decode, whole (all heads, all keys); "
+                             f"fp64 numpy oracle; {by:.3g} algorithmic bytes"}
+            if not do_prefill:
+                cpu.update(value=val / 1e9, unit="GB/s", sample=cpu["decode"]["sample"])
 
     props = torch.cuda.get_device_properties(dev)
     line = {
@@ -311,6 +397,10 @@ def main():
             "prefill_attend_ms_median_min": [round(median(attn), 3), round(min(attn), 3)] if do_prefill else None,
             "decode_ms_median_min": [round(median(dec), 4), round(min(dec), 4)] if do_decode else None,
             "decode_ms_median_min_50": dec50,
+            "decode_building_table_rows_ms_median_min_50": dec50_rows,
+            "decode_definition": "one step = jl_bifocal_decode_with_table (split-K kernel + combine) over a cos/sin "
+                                 "table of all 131072 positions built once before the timed region; "
+                                 "jl_bifocal_decode, which builds the rows it reads on every call, is timed beside it",
             "decode_GBps": round(dec_gbs, 1),
             "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
             "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4),
@@ -329,7 +419,7 @@ def main():
             "traffic": traffic,
         },
         "roofline_decode": {
-            "kernel": "decode (table + split + combine)",
+            "kernel": "decode (split + combine over the prepared table)",
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),
             "peak": PEAK_HBM,

@@ -34,8 +34,40 @@
  *             JL_ERR_HIP.  A device fault surfaces at the caller's next
  *             synchronisation.  No C++ exception crosses this interface.
  *   dtype:    JL_F32 (float) or JL_BF16 (bfloat16, round-to-nearest-even on
- *             output).  Accumulation, softmax and rotation run in fp32; the
- *             RoPE angles and their cos/sin are formed in fp64.
+ *             output).  The RoPE angles and their cos/sin are formed in fp64
+ *             and rounded once to fp32.
+ *             JL_F32: rotation, products, softmax and accumulation in fp32.
+ *             JL_BF16: the matrix-core operands are IEEE half (f16), every
+ *             product is accumulated in fp32:
+ *               prefill - each key is rotated once in fp32 and stored as
+ *                 half; values are converted to half (exact for bf16 in
+ *                 range); queries are rotated in fp32, scaled by
+ *                 softmax_scale * log2(e) and rounded to half; the
+ *                 probabilities are rounded to half, and each row's sum of
+ *                 them is formed per 64-key tile by a tree of packed-half
+ *                 adds (relative error below 2^-11 per level) before it is
+ *                 added to the fp32 running sum; maxima, exponentials and
+ *                 rescaling run in fp32.
+ *               decode - each key is converted to half and rotated in
+ *                 packed-half arithmetic from a half copy of its cos/sin row;
+ *                 the query as in prefill; P V runs on the bf16 matrix cores
+ *                 with P split into a bf16 high and low part (about 16
+ *                 significant bits) against the exact bf16 values; softmax
+ *                 and accumulation in fp32.  With JL_FLAG_PREROTATED and
+ *                 w0 >= max_L (every key inside the window: plain RoPE
+ *                 attention over a RoPE cache) Q K^T runs on the bf16 matrix
+ *                 cores straight from the stored keys, the scaled query
+ *                 rounded to bf16.
+ *   Range (JL_BF16): half holds magnitudes below 65520.  Supported inputs:
+ *             |k_e| < 46300 for every key element (each rotated component
+ *             then stays below its pair's norm, < 65504), |v_e| < 65504 for
+ *             prefill values, |q_e| * softmax_scale * log2(e) < 46300 for
+ *             queries; decode values are not limited.  A rotated key, value
+ *             or scaled query outside half range is replaced by NaN (decode:
+ *             its scores become infinite or NaN and the head's result is set
+ *             to NaN), so the outputs that attend it come out NaN, never as
+ *             a wrong finite value; other rows of the same sequence and KV
+ *             head may be NaN too.
  *   head_dim: 64 or 128.  Hq must be a multiple of Hkv.
  *   Limits:   sequence lengths < 2^31; positions are int32.  bf16 prefill
  *             (prepare and attend): (roundup64(total_k) + 64 B) * head_dim
@@ -230,6 +262,53 @@ int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
                          double rope_theta, float softmax_scale,
                          void* workspace, size_t workspace_bytes, void* stream, unsigned flags);
+
+/* Prepared cos/sin table for jl_bifocal_decode_with_table: the angles p *
+ * theta_k of positions p = 0 .. max_pos-1 (theta_k = theta^(-2k/d)), formed
+ * in fp64; fp32 (cos, sin) rows [max_pos][head_dim/2], then, 256-byte
+ * aligned, half rows [max_pos][head_dim] holding (cos, cos, sin, sin) of
+ * each frequency pair.  It depends only on max_pos, head_dim and theta, so a
+ * caller builds it once (as a RoPE cos/sin cache) and reuses it for every
+ * decode step.  jl_bifocal_rope_table_size returns its bytes (0 on invalid
+ * sizes); jl_bifocal_rope_table fills caller-owned device memory (256-byte
+ * aligned, >= that size) on `stream`. */
+size_t jl_bifocal_rope_table_size(int max_pos, int head_dim);
+int jl_bifocal_rope_table(int max_pos, int head_dim, double rope_theta, void* table, size_t table_bytes,
+                          void* stream);
+
+/* jl_bifocal_decode_ex over a prepared table instead of building the cos/sin
+ * rows it reads on every call ("Inference Efficiency Mechanisms": the
+ * rotations are applied on the fly; the cos/sin values themselves do not
+ * depend on the call).  table: device, from jl_bifocal_rope_table with the
+ * same head_dim and the rope_theta wanted (not checked: a different theta
+ * gives a different, valid-looking result), covering table_rows >= max_L
+ * positions; table_bytes its size.  It is read only (and not read at all by a
+ * bf16 pre-rotated call with w0 >= max_L).  workspace: device, 256-byte
+ * aligned, >= jl_bifocal_decode_with_table_workspace_size(...) bytes (the
+ * partial states of the key-range splits).  Everything else, including
+ * flags, as jl_bifocal_decode_ex. */
+size_t jl_bifocal_decode_with_table_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv,
+                                                   int head_dim);
+int jl_bifocal_decode_with_table(const void* q, const void* k_cache, const void* v_cache,
+                                 int64_t stride_b, int64_t stride_s, int64_t stride_h,
+                                 void* o, float* lse, int dtype, const int32_t* seq_L, int B,
+                                 int max_L, int Hq, int Hkv, int head_dim, int w_pretrained, int w0,
+                                 float softmax_scale, const void* table, size_t table_bytes,
+                                 int table_rows, void* workspace, size_t workspace_bytes,
+                                 void* stream, unsigned flags);
+
+/* Debug export of the bf16 decode's integer map ("Dynamic Bifocal RoPE",
+ * eq. G / eq. f): for sequence b (seq_L device int32 [B]) and key j <
+ * seq_L[b], rows_out[b * max_L + j] (device int32 [B, max_L]) receives the
+ * cos/sin row the bf16 split kernel rotates key j with, computed by the same
+ * device code and key walk as that kernel for these B, max_L and Hkv: j if
+ * the key is within w0 of the query at seq_L[b]-1, else f(j) = floor(j / G);
+ * with JL_FLAG_PREROTATED 0 for a local key and ~(j - f(j)) (the correction
+ * R(f(j) - j): row j - f(j) with sin negated, stored bit-inverted) for a
+ * remote one.  Entries j >= seq_L[b], and sequences outside 1 .. max_L, are
+ * not written. */
+int jl_bifocal_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained,
+                               int w0, unsigned flags, int32_t* rows_out, void* stream);
 
 /* Integer position map of a packed batch, exactly as the prefill kernels use
  * it (eq. G, eq. f).  Device outputs: pos_out/f_out int32 [total_q] (query

@@ -162,3 +162,46 @@ def test_prefill_ie_workspace_and_rejections():
     bad[15] = 96
     assert L.jl_bifocal_prefill_ie(*bad, 0) == -2
     assert L.jl_bifocal_prefill_ie(*args, 4) == -1 and b"flag" in L.jl_last_error()
+
+
+def _decode_table(L, **kw):
+    a = dict(q=256, kc=256, vc=256, sb=1 << 20, ss=1024, sh=128, o=1, lse=None, dtype=jl.JL_BF16,
+             seq_L=1, B=2, max_L=64, Hq=8, Hkv=2, d=128, wp=32, w0=4, scale=0.0, tab=256, tab_bytes=1 << 40,
+             tab_rows=64, ws=256, ws_bytes=1 << 40, flags=0)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return L.jl_bifocal_decode_with_table(vp(a["q"]), vp(a["kc"]), vp(a["vc"]), a["sb"], a["ss"], a["sh"],
+                                          vp(a["o"]), vp(a["lse"]), a["dtype"], vp(a["seq_L"]), a["B"],
+                                          a["max_L"], a["Hq"], a["Hkv"], a["d"], a["wp"], a["w0"], a["scale"],
+                                          vp(a["tab"]), a["tab_bytes"], a["tab_rows"], vp(a["ws"]),
+                                          a["ws_bytes"], None, a["flags"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tab=None), -1), (dict(tab_rows=63), -1), (dict(tab_bytes=100), -1), (dict(tab=257), -1),
+    (dict(ws=None), -3), (dict(ws_bytes=8), -3), (dict(flags=2), -1), (dict(d=96), -2), (dict(Hq=9), -1),
+])
+def test_decode_with_table_rejects_before_any_launch(kw, code):
+    L = _lib()
+    assert _decode_table(L, **kw) == code
+    assert L.jl_last_error().decode() != ""
+
+
+def test_rope_table_and_key_rows_reject_bad_args():
+    L = _lib()
+    vp = ctypes.c_void_p
+    assert jl.rope_table_size(131072, 128) == 131072 * 64 * 8 + 131072 * 128 * 2
+    assert jl.rope_table_size(10, 96) == 0
+    assert L.jl_bifocal_rope_table(100, 96, 1e4, vp(256), 1 << 30, None) == -2
+    assert L.jl_bifocal_rope_table(100, 128, 0.0, vp(256), 1 << 30, None) == -1
+    assert L.jl_bifocal_rope_table(100, 128, 1e4, None, 1 << 30, None) == -1
+    assert L.jl_bifocal_rope_table(100, 128, 1e4, vp(256), 16, None) == -1
+    assert L.jl_bifocal_rope_table(0, 128, 1e4, None, 0, None) == 0
+    assert L.jl_bifocal_decode_key_rows(vp(1), 1, 10, 0, 4, 1, 0, vp(1), None) == -1
+    assert L.jl_bifocal_decode_key_rows(vp(1), 1, 10, 2, 0, 1, 0, vp(1), None) == -1
+    assert L.jl_bifocal_decode_key_rows(None, 1, 10, 2, 4, 1, 0, vp(1), None) == -1
+    assert L.jl_bifocal_decode_key_rows(vp(1), 1, 10, 2, 4, 1, 4, vp(1), None) == -1
+    assert L.jl_bifocal_decode_key_rows(None, 0, 10, 2, 4, 1, 0, None, None) == 0
+    # partial states only: far below the decode workspace that also holds the table rows
+    assert 0 < jl.decode_with_table_workspace_size(jl.JL_BF16, 16, 131072, 32, 8, 128) < \
+        jl.decode_workspace_size(jl.JL_BF16, 16, 131072, 32, 8, 128) - 131072 * 64 * 8

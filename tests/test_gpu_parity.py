@@ -344,7 +344,7 @@ def test_decode_invalid_lengths_left_unwritten(dt):
 
 def test_decode_strided_cache_and_untouched():
     """A cache laid out [S, B, Hkv, d] (non-default strides) is read in place
-    and left byte-identical."""
+    and both caches are left byte-identical."""
     torch = _torch()
     _say("decode strided")
     B, S, Hq, Hkv, d = 3, 1200, 8, 2, 128
@@ -353,10 +353,11 @@ def test_decode_strided_cache_and_untouched():
     v = W.to_device(inp["v"], "bf16").permute(1, 0, 2, 3).contiguous().permute(1, 0, 2, 3)
     q = W.to_device(inp["q"], "bf16")
     seq = torch.from_numpy(inp["seq_L"]).cuda()
-    hk = hashlib.sha256(k.contiguous().view(torch.int16).cpu().numpy().tobytes()).hexdigest()
+    digest = lambda t: hashlib.sha256(t.contiguous().view(torch.int16).cpu().numpy().tobytes()).hexdigest()  # noqa: E731
+    hk, hv = digest(k), digest(v)
     out = jl.decode(q, k, v, seq, 256, 100, 1e4)
     torch.cuda.synchronize()
-    assert hashlib.sha256(k.contiguous().view(torch.int16).cpu().numpy().tobytes()).hexdigest() == hk
+    assert digest(k) == hk and digest(v) == hv
     o_ref, _ = oracle.bifocal_decode(W.as_f64(inp["q"], "bf16"), W.as_f64(inp["k"], "bf16"),
                                      W.as_f64(inp["v"], "bf16"), inp["seq_L"], 256, 100, 1e4)
     err = np.max(np.abs(out.float().cpu().numpy() - o_ref))

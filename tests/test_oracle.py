@@ -76,6 +76,26 @@ def test_group_size_rejects_bad_args():
 
 # ---------------------------------------------------------------- rotation
 
+def test_rope_frequencies_golden():
+    """theta_k at every k (not only k = 0) against hand-derived powers of ten."""
+    for c in _load("rope_pairs.json")["frequencies"]:
+        got = oracle.rope_frequencies(c["d"], c["theta"])
+        assert np.allclose(got, c["theta_k"], rtol=1e-14, atol=0), (c, got)
+
+
+def test_rope_rotation_golden_higher_pairs():
+    """R(p) of a one-hot vector in a pair k >= 1 lands on (cos a, sin a) at the
+    pair's two features, a = p * theta_k a whole number of radians."""
+    for c in _load("rope_pairs.json")["rotations"]:
+        x = np.zeros((1, c["d"]))
+        x[0, c["one_hot"]] = 1.0
+        got = oracle.rope_rotate(x, [c["p"]], c["theta"])[0]
+        want = np.zeros(c["d"])
+        want[c["cos_at"]] = math.cos(c["angle_rad"])
+        want[c["sin_at"]] = c.get("sin_sign", 1) * math.sin(c["angle_rad"])
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (c, got)
+
+
 def test_rope_matches_complex_form():
     rng = np.random.default_rng(0)
     for d in (2, 8, 64, 128):

@@ -19,6 +19,7 @@ __all__ = [
     "group_size", "prefill", "prefill_prepare", "prefill_attend", "prefill_ie", "decode", "prefill_workspace_size",
     "prefill_ie_workspace_size", "decode_workspace_size",
     "remote_positions", "tile_classes", "prefill_tile_shape", "version",
+    "rope_table", "rope_table_size", "decode_with_table", "decode_with_table_workspace_size", "decode_key_rows",
 ]
 
 JL_F32, JL_BF16 = 0, 1
@@ -77,6 +78,17 @@ def lib() -> ctypes.CDLL:
     L.jl_bifocal_prefill_ie_workspace_size.restype = c_sz
     L.jl_bifocal_prefill_ie.argtypes = L.jl_bifocal_prefill_ex.argtypes
     L.jl_bifocal_prefill_ie.restype = c_int
+    L.jl_bifocal_rope_table_size.argtypes = [c_int, c_int]
+    L.jl_bifocal_rope_table_size.restype = c_sz
+    L.jl_bifocal_rope_table.argtypes = [c_int, c_int, c_d, c_vp, c_sz, c_vp]
+    L.jl_bifocal_rope_table.restype = c_int
+    L.jl_bifocal_decode_with_table_workspace_size.argtypes = [c_int] * 6
+    L.jl_bifocal_decode_with_table_workspace_size.restype = c_sz
+    L.jl_bifocal_decode_with_table.argtypes = ([c_vp] * 3 + [c_i64] * 3 + [c_vp, c_vp, c_int, c_vp] +
+                                               [c_int] * 7 + [c_f, c_vp, c_sz, c_int, c_vp, c_sz, c_vp, c_u])
+    L.jl_bifocal_decode_with_table.restype = c_int
+    L.jl_bifocal_decode_key_rows.argtypes = [c_vp] + [c_int] * 5 + [c_u, c_vp, c_vp]
+    L.jl_bifocal_decode_key_rows.restype = c_int
     L.jl_bifocal_remote_positions.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     L.jl_bifocal_remote_positions.restype = c_int
     L.jl_bifocal_tile_classes.argtypes = [c_int] * 5 + [c_vp, c_vp]
@@ -296,6 +308,74 @@ def decode(q, k_cache, v_cache, seq_L, w_pretrained: int, w0: int, rope_theta: f
         JL_FLAG_PREROTATED if prerotated else 0)
     _check(code)
     return (out, lse) if return_lse else out
+
+
+def rope_table_size(max_pos: int, head_dim: int) -> int:
+    return int(lib().jl_bifocal_rope_table_size(int(max_pos), int(head_dim)))
+
+
+def rope_table(max_pos: int, head_dim: int, rope_theta: float, device="cuda", table=None):
+    """Prepared cos/sin table of positions 0 .. max_pos-1 (uint8 cuda tensor)
+    for ``decode_with_table``; build once, reuse for every decode step."""
+    torch = _torch()
+    need = rope_table_size(max_pos, head_dim)
+    if table is None or table.numel() < need:
+        table = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _check(lib().jl_bifocal_rope_table(int(max_pos), int(head_dim), float(rope_theta), _ptr(table), table.numel(),
+                                       _stream(table.device)))
+    return table
+
+
+def decode_with_table_workspace_size(dtype: int, B: int, max_L: int, Hq: int, Hkv: int, head_dim: int) -> int:
+    return int(lib().jl_bifocal_decode_with_table_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim))
+
+
+def decode_with_table(q, k_cache, v_cache, seq_L, w_pretrained: int, w0: int, table, table_rows: int,
+                      max_L: int | None = None, softmax_scale: float = 0.0, out=None, lse=None, workspace=None,
+                      return_lse: bool = False, prerotated: bool = False):
+    """``decode`` reading a prepared cos/sin table (``rope_table``) that covers
+    ``table_rows`` >= max_L positions and was built with the wanted theta."""
+    torch = _torch()
+    _need_cuda(q, k_cache, v_cache, seq_L, table)
+    if seq_L.dtype != torch.int32:
+        raise TypeError("seq_L must be int32")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_cache.stride(3) != 1 or not q.is_contiguous():
+        raise ValueError("head_dim must be contiguous")
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    _, S, Hkv, _ = k_cache.shape
+    if max_L is None:
+        max_L = S
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = decode_with_table_workspace_size(dt, B, max_L, Hq, Hkv, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    sb, ss, sh, _ = k_cache.stride()
+    _check(lib().jl_bifocal_decode_with_table(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), sb, ss, sh, _ptr(out), _ptr(lse), dt, _ptr(seq_L),
+        B, int(max_L), Hq, Hkv, d, int(w_pretrained), int(w0), float(softmax_scale), _ptr(table), table.numel(),
+        int(table_rows), _ptr(workspace), workspace.numel(), _stream(q.device),
+        JL_FLAG_PREROTATED if prerotated else 0))
+    return (out, lse) if return_lse else out
+
+
+def decode_key_rows(seq_L, max_L: int, Hkv: int, w_pretrained: int, w0: int, prerotated: bool = False):
+    """int32 cuda [B, max_L]: the signed cos/sin row the bf16 decode kernel
+    rotates each key with (~r for row r with sin negated); entries past
+    seq_L[b] are -2**31 (not written by the library)."""
+    torch = _torch()
+    _need_cuda(seq_L)
+    B = seq_L.numel()
+    out = torch.full((max(B, 1), max(int(max_L), 1)), -2 ** 31, dtype=torch.int32, device=seq_L.device)
+    _check(lib().jl_bifocal_decode_key_rows(_ptr(seq_L), B, int(max_L), int(Hkv), int(w_pretrained), int(w0),
+                                            JL_FLAG_PREROTATED if prerotated else 0, _ptr(out),
+                                            _stream(seq_L.device)))
+    return out[:B, :max_L]
 
 
 def remote_positions(cu_seqlens_q, w_pretrained: int, cu_seqlens_k=None):

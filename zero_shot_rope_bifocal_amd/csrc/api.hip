@@ -226,11 +226,17 @@ size_t jl_bifocal_decode_workspace_size(int dtype, int B, int max_L, int Hq, int
   return jl::decode_ws_bytes(B, max_L, Hq, Hkv, head_dim);
 }
 
-int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
-                         int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
-                         const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
-                         int w_pretrained, int w0, double rope_theta, float softmax_scale,
-                         void* workspace, size_t workspace_bytes, void* stream, unsigned flags) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments every decode entry point shares and fills `c`
+// (workspace, table and partial-state pointers are left to the caller).
+int decode_args(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b, int64_t stride_s,
+                int64_t stride_h, void* o, float* lse, int dtype, const int32_t* seq_L, int B, int max_L, int Hq,
+                int Hkv, int head_dim, int w_pretrained, int w0, double rope_theta, float softmax_scale,
+                unsigned flags, jl::DecodeCall* c) {
+  *c = jl::DecodeCall{};
   if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   int st = check_common(dtype, Hq, Hkv, head_dim, w_pretrained, w0, rope_theta, softmax_scale);
   if (st != JL_OK) return st;
@@ -247,23 +253,107 @@ int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache
   if ((dtype == JL_BF16 && (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16 ||
                             reinterpret_cast<uintptr_t>(q) % 16)))
     return fail(JL_ERR_INVALID_ARG, "bf16 q and caches must be 16-byte aligned");
-  const size_t need = jl_bifocal_decode_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim);
+  c->q = q; c->kc = k_cache; c->vc = v_cache;
+  c->sb = stride_b; c->ss = stride_s; c->sh = stride_h;
+  c->o = o; c->lse = lse; c->seq_L = seq_L;
+  c->B = B; c->max_L = max_L; c->Hq = Hq; c->Hkv = Hkv; c->D = head_dim;
+  c->w_pretrained = w_pretrained; c->w0 = w0;
+  c->theta = rope_theta;
+  c->scale = resolve_scale(softmax_scale, head_dim);
+  c->prerot = (flags & JL_FLAG_PREROTATED) != 0;
+  return JL_OK;
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
   if (!workspace) return fail(JL_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return JL_OK;
+}
 
-  jl::DecodeCall c{};
-  c.q = q; c.kc = k_cache; c.vc = v_cache;
-  c.sb = stride_b; c.ss = stride_s; c.sh = stride_h;
-  c.o = o; c.lse = lse; c.seq_L = seq_L;
-  c.B = B; c.max_L = max_L; c.Hq = Hq; c.Hkv = Hkv; c.D = head_dim;
-  c.w_pretrained = w_pretrained; c.w0 = w0;
-  c.theta = rope_theta;
-  c.scale = resolve_scale(softmax_scale, head_dim);
+}  // namespace
+
+extern "C" {
+
+int jl_bifocal_decode_ex(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
+                         int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
+                         const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
+                         int w_pretrained, int w0, double rope_theta, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream, unsigned flags) {
+  jl::DecodeCall c;
+  int st = decode_args(q, k_cache, v_cache, stride_b, stride_s, stride_h, o, lse, dtype, seq_L, B, max_L, Hq, Hkv,
+                       head_dim, w_pretrained, w0, rope_theta, softmax_scale, flags, &c);
+  if (st != JL_OK || c.B == 0) return st;
+  st = check_workspace(workspace, workspace_bytes,
+                       jl_bifocal_decode_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim));
+  if (st != JL_OK) return st;
   c.ws = workspace;
-  c.prerot = (flags & JL_FLAG_PREROTATED) != 0;
   return hip_status(jl::launch_decode(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
                     "jl_bifocal_decode launch");
+}
+
+size_t jl_bifocal_rope_table_size(int max_pos, int head_dim) {
+  if (max_pos < 0 || !supported_dim(head_dim)) return 0;
+  return jl::rope_table_bytes(max_pos, head_dim);
+}
+
+int jl_bifocal_rope_table(int max_pos, int head_dim, double rope_theta, void* table, size_t table_bytes,
+                          void* stream) {
+  if (!supported_dim(head_dim)) return fail(JL_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (max_pos < 0) return fail(JL_ERR_INVALID_ARG, "max_pos must be non-negative");
+  if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return fail(JL_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (max_pos == 0) return JL_OK;
+  const size_t need = jl::rope_table_bytes(max_pos, head_dim);
+  if (!table) return fail(JL_ERR_INVALID_ARG, "table is NULL (%zu bytes needed)", need);
+  if (table_bytes < need) return fail(JL_ERR_INVALID_ARG, "table has %zu bytes, %zu needed", table_bytes, need);
+  if (reinterpret_cast<uintptr_t>(table) % 256) return fail(JL_ERR_INVALID_ARG, "table must be 256-byte aligned");
+  return hip_status(jl::launch_rope_table_full(table, max_pos, head_dim, rope_theta, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_rope_table launch");
+}
+
+size_t jl_bifocal_decode_with_table_workspace_size(int dtype, int B, int max_L, int Hq, int Hkv, int head_dim) {
+  if (!supported_dtype(dtype) || !supported_dim(head_dim) || B < 0 || max_L < 0 || Hq < 1 || Hkv < 1)
+    return 0;
+  return jl::decode_part_bytes(dtype == JL_BF16, B, max_L, Hq, Hkv, head_dim);
+}
+
+int jl_bifocal_decode_with_table(const void* q, const void* k_cache, const void* v_cache, int64_t stride_b,
+                                 int64_t stride_s, int64_t stride_h, void* o, float* lse, int dtype,
+                                 const int32_t* seq_L, int B, int max_L, int Hq, int Hkv, int head_dim,
+                                 int w_pretrained, int w0, float softmax_scale, const void* table,
+                                 size_t table_bytes, int table_rows, void* workspace, size_t workspace_bytes,
+                                 void* stream, unsigned flags) {
+  jl::DecodeCall c;
+  int st = decode_args(q, k_cache, v_cache, stride_b, stride_s, stride_h, o, lse, dtype, seq_L, B, max_L, Hq, Hkv,
+                       head_dim, w_pretrained, w0, 1.0, softmax_scale, flags, &c);
+  if (st != JL_OK || c.B == 0) return st;
+  if (!table) return fail(JL_ERR_INVALID_ARG, "table must be non-null");
+  if (table_rows < max_L) return fail(JL_ERR_INVALID_ARG, "table covers %d positions, max_L = %d", table_rows, max_L);
+  if (table_bytes < jl::rope_table_bytes(table_rows, head_dim))
+    return fail(JL_ERR_INVALID_ARG, "table has %zu bytes, %d rows need %zu", table_bytes, table_rows,
+                jl::rope_table_bytes(table_rows, head_dim));
+  if (reinterpret_cast<uintptr_t>(table) % 256) return fail(JL_ERR_INVALID_ARG, "table must be 256-byte aligned");
+  st = check_workspace(workspace, workspace_bytes,
+                       jl_bifocal_decode_with_table_workspace_size(dtype, B, max_L, Hq, Hkv, head_dim));
+  if (st != JL_OK) return st;
+  c.ws = workspace;
+  c.table = table;
+  c.table_rows = table_rows;
+  return hip_status(jl::launch_decode(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_decode_with_table launch");
+}
+
+int jl_bifocal_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,
+                               unsigned flags, int32_t* rows_out, void* stream) {
+  if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (B < 0 || max_L < 0 || Hkv < 1) return fail(JL_ERR_INVALID_ARG, "need B >= 0, max_L >= 0, Hkv >= 1");
+  if (w_pretrained < 1 || w0 < 0) return fail(JL_ERR_INVALID_ARG, "need w_pretrained >= 1 and w0 >= 0");
+  if (B == 0 || max_L == 0) return JL_OK;
+  if (!seq_L || !rows_out) return fail(JL_ERR_INVALID_ARG, "seq_L and rows_out must be non-null");
+  return hip_status(jl::launch_decode_key_rows(seq_L, B, max_L, Hkv, w_pretrained, w0,
+                                               (flags & JL_FLAG_PREROTATED) != 0, rows_out,
+                                               static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_decode_key_rows launch");
 }
 
 int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,

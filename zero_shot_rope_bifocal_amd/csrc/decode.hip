@@ -27,6 +27,8 @@
 //     high and low part so that P V keeps ~16 bits of P on exact bf16 V.
 //   fp32: the same stream with the products on the VALU (4 wavefronts).
 // Kernel 2 (combine): log-sum-exp merge of the per-wavefront partials.
+#include <algorithm>
+
 #include "jl_device.hpp"
 #include "jl_launch.hpp"
 
@@ -53,6 +55,7 @@ struct Params {
   int w_pretrained, w0;
   float scale_log2;
   int prerot;  // q and the key cache arrive rotated at their true positions
+  int plain;   // bf16, pre-rotated, every key inside the window (kKeyPlain)
 };
 
 template <int D>
@@ -113,6 +116,52 @@ __device__ __forceinline__ float xrow_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Blocks of one wavefront: j0 = kbeg + w*16 + n*step over its key range,
+// with j0 / G tracked as a quotient q0 and remainder r0 (no integer division
+// in the loop).  The debug export of the key rows walks the same blocks.
+struct KeyBlocks {
+  int j0, q0, r0, qs, rs, step, G;
+  __device__ __forceinline__ KeyBlocks(int kbeg, int w, int wph, int G_) : G(G_) {
+    step = wph * 16;
+    qs = step / G;
+    rs = step % G;
+    j0 = kbeg + w * 16;
+    q0 = j0 / G;
+    r0 = j0 % G;
+  }
+  __device__ __forceinline__ void next() {
+    j0 += step;
+    q0 += qs;
+    r0 += rs;
+    if (r0 >= G) {
+      r0 -= G;
+      ++q0;
+    }
+  }
+};
+
+// Table row and sign of sin with which the bf16 split kernel rotates key
+// jk = j0 + col (col < 16) of a block that starts at j0 = q0 * G + r0: j if the
+// key is within w0 of the query at qpos, else f(j) = j / G (eq. f).  Outside
+// the tail, f(j) = q0 + (r0 + col) / G with the small quotient taken in fp32:
+// (n + 1/2) / G lies at least 1/(2G) from an integer and the product with the
+// rounded reciprocal errs by under (G + 16) 2^-23 / G, so the truncation is
+// exact for G < 2^20 (above, an integer division).  In a tail block
+// (TAIL) keys at or past kend read row 0.  PR (pre-rotated cache): a local
+// key is used as stored (row 0: cos 1, sin 0), a remote one gets the
+// correction R(f(j) - j), i.e. row j - f(j) with sin negated.
+template <bool PR, bool TAIL>
+__device__ __forceinline__ RotRow split_key_rot(int jk, int col, int q0, int r0, int G, float invG, int qpos,
+                                                int w0, int kend) {
+  const bool klocal = qpos - jk < w0;
+  int fj;
+  if constexpr (TAIL) fj = jk / G;
+  else fj = G < (1 << 20) ? q0 + static_cast<int>((static_cast<float>(r0 + col) + 0.5f) * invG) : jk / G;
+  int row = klocal ? (PR ? 0 : jk) : (PR ? jk - fj : fj);
+  if constexpr (TAIL) row = jk < kend ? row : 0;
+  return RotRow{row, PR && !klocal ? -1.f : 1.f};
+}
+
 // Loop-invariant state of one wavefront of the bf16 split kernel.
 template <int D>
 struct SplitCtx {
@@ -137,12 +186,21 @@ template <int D>
 struct SplitState {
   f32x4 o[D / 16];
   float m, l;
+  bool bad;  // some key of this lane's head scored -inf: an input outside half range
 };
+
+// How the bf16 split kernel treats the keys it streams.  kKeyRaw: raw keys,
+// rotated at j or f(j) from the half cos/sin rows.  kKeyPre: a pre-rotated
+// cache, local keys used as stored and remote keys corrected by R(f(j) - j).
+// kKeyPlain: a pre-rotated cache with every key inside the window (w0 >=
+// max_L), i.e. plain RoPE attention over a RoPE cache: no table, no key
+// rotation, Q K^T straight from the stored bf16 keys on the bf16 MFMA.
+enum : int { kKeyRaw = 0, kKeyPre = 1, kKeyPlain = 2 };
 
 // One 16-key block starting at j0 (wave-uniform).  q0 = j0 / G, r0 = j0 % G.
 // TAIL: the block may run past kend; rows are clamped to kend-1 and their
 // probabilities are zero.
-template <int D, int NR, bool TAIL, bool PR>
+template <int D, int NR, bool TAIL, int KM>
 __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&qrf)[D / 32],
                                             SplitState<D>& st, int j0, int q0, int r0) {
   constexpr int NT = D / 32;
@@ -151,6 +209,7 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   constexpr int NB = D / 16;
   constexpr int CPR = D / 8;
   constexpr int RPI = 64 / CPR;  // V rows per LDS-load instruction
+  constexpr bool PR = KM == kKeyPre;
   const int col = c.col, g = c.g;
 
   // ---- K in the A layout (lane = key j0 + col, features t*32 + g*8 ..) and
@@ -175,28 +234,17 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     load_lds16(src, c.vblk + t * 512);
   }
 
-  // ---- rotate each key at its own angle: j if within w0 of the query,
-  // else f(j) = j / G = q0 + (r0 + col) / G.  The small quotient is exact in
-  // fp32: (n + 1/2) / G lies at least 1/(2G) from an integer and the product
-  // with the rounded reciprocal errs by under (G + 16) 2^-23 / G.  Rows past
-  // kend (tail only) read table row 0.
-  // PR (pre-rotated cache): local keys are used as stored (row 0: cos 1,
-  // sin 0) and remote keys get R(f(j) - j), i.e. row j - f(j) with sin negated
-  const bool klocal = c.qpos - jk < c.w0;
-  int kpos;
-  if constexpr (TAIL) {
-    const int fj = jk / c.G;
-    kpos = jk < c.kend ? (klocal ? (PR ? 0 : jk) : (PR ? jk - fj : fj)) : 0;
-  } else {
-    const int frem = c.G < (1 << 20) ? q0 + static_cast<int>((static_cast<float>(r0 + col) + 0.5f) * c.invG)
-                                     : jk / c.G;
-    kpos = klocal ? (PR ? 0 : jk) : (PR ? jk - frem : frem);
-  }
-  const float ksgn = PR && !klocal ? -1.f : 1.f;
+  f16x8 a[NT];
+  if constexpr (KM != kKeyPlain) {
+  // ---- rotate each key at its own angle (split_key_rot)
+  const RotRow krot = split_key_rot<PR, TAIL>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
+  const int kpos = krot.row;
+  const float ksgn = krot.sgn;
   // rotation in packed half: the bf16 key converts to half exactly, the half
   // cos/sin carry at most 2^-12 absolute error, and the result is rounded to
-  // half for the MFMA either way
-  f16x8 a[NT];
+  // half for the MFMA either way.  A key outside half range turns into
+  // +-inf here, its scores into +-inf or NaN (never finite); NaN and +inf
+  // poison the head's sums by themselves, -inf is caught below.
   const uint4* cs8 = reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(kpos) * (H / 2) + g * 4) * 4);
   const f16x2 sgn2 = {static_cast<_Float16>(ksgn), static_cast<_Float16>(ksgn)};
 #pragma unroll
@@ -221,16 +269,23 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
       a[t + HT][2 * e2 + 1] = o2[1];
     }
   }
+  }
 
   // ---- S = K_rot Q_sel^T: lane (col = head, g) holds keys j0 + g*4 + rr
   const bool all_remote = c.qpos - (j0 + kKB - 1) >= c.w0;
   const bool all_local = c.qpos - j0 < c.w0;
   f32x4 sr = {0.f, 0.f, 0.f, 0.f}, sl = {0.f, 0.f, 0.f, 0.f};
-  if (!all_local) {
+  if constexpr (KM == kKeyPlain) {
+    // every key local: the stored bf16 key is the A operand as loaded
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t]), __builtin_bit_cast(bf16x8, qrf[t]),
+                                                   sl, 0, 0, 0);
+  } else if (!all_local) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qrf[t], sr, 0, 0, 0);
   }
-  if (!all_remote) {
+  if (KM != kKeyPlain && !all_remote) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], c.ql[(t * 4 + g) * NR + c.qcol], sl, 0, 0, 0);
@@ -238,12 +293,18 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   // one logit set per key: outside the window edge the other set was not
   // formed and is zero
   float sv[4];
-  if (all_remote || all_local) {
+  if (KM == kKeyPlain || all_remote || all_local) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) sv[rr] = sr[rr] + sl[rr];
   } else {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) sv[rr] = c.qpos - (j0 + g * 4 + rr) < c.w0 ? sl[rr] : sr[rr];
+  }
+  if constexpr (KM != kKeyPlain) {
+    // a finite in-range key never scores -inf; one that does was outside
+    // half range (see above) and makes its head's result NaN at the end
+    const float lmin = fminf(fminf(sv[0], sv[1]), fminf(sv[2], sv[3]));
+    st.bad = st.bad || lmin == -INFINITY;
   }
   if constexpr (TAIL) {
 #pragma unroll
@@ -297,8 +358,9 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   }
 }
 
-template <int D, int NR, bool PR>
+template <int D, int NR, int KM>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void split_bf16_kernel(Params p) {
+  constexpr bool PR = KM == kKeyPre;
   constexpr int NT = D / 32;    // QK^T MFMAs per 16 keys (32 features each)
   constexpr int HT = NT / 2;    // first-half feature groups
   constexpr int H = D / 2;
@@ -377,28 +439,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
     }
-    const RotRow rl = rot_row(qpos, qpos, PR);
-    const RotRow rr = rot_row(qpos / G, qpos, PR);
     const float sc = p.scale_log2;
-    f16x8 ql[NT];
+    if constexpr (KM == kKeyPlain) {
+      // stored query (already rotated at qpos), scaled, as a bf16 operand
 #pragma unroll
-    for (int t = 0; t < HT; ++t)
+      for (int t = 0; t < NT; ++t) {
+        bf16x8 qb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = t * 32 + g * 8 + e;
-        float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
-        float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
-        cl.y *= rl.sgn;
-        cr.y *= rr.sgn;
-        const float x1 = x[t][e], x2 = x[t + HT][e];
-        ql[t][e] = static_cast<_Float16>((x1 * cl.x - x2 * cl.y) * sc);
-        ql[t + HT][e] = static_cast<_Float16>((x2 * cl.x + x1 * cl.y) * sc);
-        qrf[t][e] = static_cast<_Float16>((x1 * cr.x - x2 * cr.y) * sc);
-        qrf[t + HT][e] = static_cast<_Float16>((x2 * cr.x + x1 * cr.y) * sc);
+        for (int e = 0; e < 8; ++e) qb[e] = static_cast<__bf16>(x[t][e] * sc);
+        qrf[t] = __builtin_bit_cast(f16x8, qb);
       }
-    if (col < NR) {
+    } else {
+      const RotRow rl = rot_row(qpos, qpos, PR);
+      const RotRow rr = rot_row(qpos / G, qpos, PR);
+      f16x8 ql[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sQl[wid][(t * 4 + g) * NR + col] = ql[t];
+      for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kk = t * 32 + g * 8 + e;
+          float2 cl = p.tab[static_cast<int64_t>(rl.row) * H + kk];
+          float2 cr = p.tab[static_cast<int64_t>(rr.row) * H + kk];
+          cl.y *= rl.sgn;
+          cr.y *= rr.sgn;
+          const float x1 = x[t][e], x2 = x[t + HT][e];
+          ql[t][e] = half_or_nan((x1 * cl.x - x2 * cl.y) * sc);
+          ql[t + HT][e] = half_or_nan((x2 * cl.x + x1 * cl.y) * sc);
+          qrf[t][e] = half_or_nan((x1 * cr.x - x2 * cr.y) * sc);
+          qrf[t + HT][e] = half_or_nan((x2 * cr.x + x1 * cr.y) * sc);
+        }
+      if (col < NR) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sQl[wid][(t * 4 + g) * NR + col] = ql[t];
+      }
     }
   }
 
@@ -419,20 +492,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   for (int nb = 0; nb < NB; ++nb) st.o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
+  st.bad = false;
 
-  // blocks j0 = kbeg + w*16 + n*step; j0 / G tracked as quotient + remainder
-  const int step = p.wph * kKB;
-  const int qs = step / G, rs = step % G;
-  int j0 = kbeg + w * kKB;
-  int q0 = j0 / G, r0 = j0 % G;
-  for (; j0 + kKB <= kend; j0 += step) {
-    split_block<D, NR, false, PR>(c, qrf, st, j0, q0, r0);
-    q0 += qs;
-    r0 += rs;
-    if (r0 >= G) { r0 -= G; ++q0; }
-  }
-  if (j0 < kend) split_block<D, NR, true, PR>(c, qrf, st, j0, q0, r0);
+  KeyBlocks kb(kbeg, w, p.wph, G);
+  for (; kb.j0 + kKB <= kend; kb.next()) split_block<D, NR, false, KM>(c, qrf, st, kb.j0, kb.q0, kb.r0);
+  if (kb.j0 < kend) split_block<D, NR, true, KM>(c, qrf, st, kb.j0, kb.q0, kb.r0);
 
+  if (st.bad) st.l = __builtin_nanf("");
   st.l = xrow_sum(st.l);
 
   // ---- this wavefront's partial state: O feature nb*16 + col of head
@@ -593,66 +659,112 @@ __global__ __launch_bounds__(kWavesF32 * 64) void split_f32_kernel(Params p) {
 // ---------------------------------------------------------------- combine
 
 // Log-sum-exp merge of the partial states of one (sequence, query head):
-// weights 2^(m_s - M) are formed once, then each thread sums one feature
-// over the partials (coalesced reads).
+// the weights 2^(m_s - M) are formed once into LDS; then the kCombThreads /
+// D thread groups each sum every NG-th partial state for one feature, with
+// four independent accumulators so that several loads are in flight, and
+// the group sums are added in LDS.
+constexpr int kCombThreads = 512;
+constexpr int kMaxParts = 1024;
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nparts, void* o,
-                                                    float* lse, int bf16, const int32_t* __restrict__ seq_L,
-                                                    int Hq, int max_L) {
-  constexpr int kMaxParts = 1024;
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* __restrict__ part, int nparts, void* o,
+                                                               float* lse, int bf16, const int32_t* __restrict__ seq_L,
+                                                               int Hq, int max_L) {
+  constexpr int NW = kCombThreads / 64;
+  constexpr int NG = kCombThreads / D;
   __shared__ float sw[kMaxParts];
-  __shared__ float sred[D / 64];
-  __shared__ float sM, sden;
+  __shared__ float sred_m[NW], sred_d[NW];
+  __shared__ float sacc[NG][D];
   const int bh = blockIdx.x;  // b * Hq + h
   const int t = threadIdx.x;
   const int L = seq_L[bh / Hq];
   if (L < 1 || L > max_L) return;  // outside the documented contract: left unwritten, as in the split kernel
   const float* pp = part + static_cast<int64_t>(bh) * nparts * (D + 2);
   float mx = -INFINITY;
-  for (int s = t; s < nparts; s += D) mx = fmaxf(mx, pp[s * (D + 2) + D]);
+  for (int s = t; s < nparts; s += kCombThreads) mx = fmaxf(mx, pp[s * (D + 2) + D]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((t & 63) == 0) sred[t >> 6] = mx;
+  if ((t & 63) == 0) sred_m[t >> 6] = mx;
   __syncthreads();
-  if (t == 0) {
-    float M = sred[0];
-    for (int i = 1; i < D / 64; ++i) M = fmaxf(M, sred[i]);
-    sM = M;
-  }
-  __syncthreads();
-  const float M = sM;
+  float M = sred_m[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, sred_m[i]);
   float den = 0.f;
-  for (int s = t; s < nparts; s += D) {
+  for (int s = t; s < nparts; s += kCombThreads) {
     const float ms = pp[s * (D + 2) + D];
     const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
     sw[s] = wgt;
     den += wgt * pp[s * (D + 2) + D + 1];
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  if ((t & 63) == 0) sred_d[t >> 6] = den;
   __syncthreads();
-  if ((t & 63) == 0) sred[t >> 6] = den;
-  __syncthreads();
-  if (t == 0) {
-    float dd = 0.f;
-    for (int i = 0; i < D / 64; ++i) dd += sred[i];
-    sden = dd;
+  const int f = t % D, gi = t / D;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = gi;
+  for (; s + 3 * NG < nparts; s += 4 * NG) {
+    a0 = fmaf(sw[s], pp[s * (D + 2) + f], a0);
+    a1 = fmaf(sw[s + NG], pp[(s + NG) * (D + 2) + f], a1);
+    a2 = fmaf(sw[s + 2 * NG], pp[(s + 2 * NG) * (D + 2) + f], a2);
+    a3 = fmaf(sw[s + 3 * NG], pp[(s + 3 * NG) * (D + 2) + f], a3);
   }
+  for (; s < nparts; s += NG) a0 = fmaf(sw[s], pp[s * (D + 2) + f], a0);
+  sacc[gi][f] = (a0 + a1) + (a2 + a3);
   __syncthreads();
+  if (t >= D) return;
   float num = 0.f;
-  for (int s = 0; s < nparts; ++s) num = fmaf(sw[s], pp[s * (D + 2) + t], num);
-  const float r = num / sden;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) num += sacc[i][t];
+  float dd = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) dd += sred_d[i];
+  const float r = num / dd;
   if (bf16) static_cast<uint16_t*>(o)[static_cast<int64_t>(bh) * D + t] = float_to_bf16_bits(r);
   else static_cast<float*>(o)[static_cast<int64_t>(bh) * D + t] = r;
-  if (lse && t == 0) lse[bh] = (M + log2f(sden)) * kLn2;
+  if (lse && t == 0) lse[bh] = (M + log2f(dd)) * kLn2;
+}
+
+// Debug export: the signed table row the bf16 split kernel rotates each key
+// with (split_key_rot over the same KeyBlocks walk), row r with sin negated
+// stored as ~r.  One thread per (split, wave slot, key column) of sequence
+// blockIdx.y; keys past L_b are not written.
+template <bool PR>
+__global__ void key_rows_kernel(const int32_t* __restrict__ seq_L, int max_L, int nsplit, int kps, int wph,
+                                int w_pretrained, int w0, int32_t* __restrict__ out) {
+  const int b = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int col = idx % 16;
+  const int w = (idx / 16) % wph;
+  const int split = idx / (16 * wph);
+  if (split >= nsplit) return;
+  const int L = seq_L[b];
+  if (L < 1 || L > max_L) return;
+  const int G = group_size(L, w_pretrained);
+  const float invG = 1.f / static_cast<float>(G);
+  const int qpos = L - 1;
+  const int kbeg = split * kps;
+  const int kend = min(L, kbeg + kps);
+  int32_t* dst = out + static_cast<int64_t>(b) * max_L;
+  KeyBlocks kb(kbeg, w, wph, G);
+  for (; kb.j0 + kKB <= kend; kb.next()) {
+    const RotRow r = split_key_rot<PR, false>(kb.j0 + col, col, kb.q0, kb.r0, G, invG, qpos, w0, kend);
+    dst[kb.j0 + col] = r.sgn < 0.f ? ~r.row : r.row;
+  }
+  if (kb.j0 < kend && kb.j0 + col < kend) {
+    const RotRow r = split_key_rot<PR, true>(kb.j0 + col, col, kb.q0, kb.r0, G, invG, qpos, w0, kend);
+    dst[kb.j0 + col] = r.sgn < 0.f ? ~r.row : r.row;
+  }
 }
 
 template <int D, int NR>
 void launch_split(const Params& p, bool bf16, hipStream_t s) {
   if (bf16) {
     const int hw = kWaves / p.wph;
-    if (p.prerot)
-      hipLaunchKernelGGL((split_bf16_kernel<D, NR, true>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
+    const dim3 grid(p.B * (p.Hkv / hw), p.nsplit);
+    if (p.plain)
+      hipLaunchKernelGGL((split_bf16_kernel<D, NR, kKeyPlain>), grid, dim3(kWaves * 64), 0, s, p);
+    else if (p.prerot)
+      hipLaunchKernelGGL((split_bf16_kernel<D, NR, kKeyPre>), grid, dim3(kWaves * 64), 0, s, p);
     else
-      hipLaunchKernelGGL((split_bf16_kernel<D, NR, false>), dim3(p.B * (p.Hkv / hw), p.nsplit), dim3(kWaves * 64), 0, s, p);
+      hipLaunchKernelGGL((split_bf16_kernel<D, NR, kKeyRaw>), grid, dim3(kWaves * 64), 0, s, p);
   } else {
     hipLaunchKernelGGL((split_f32_kernel<D, NR>), dim3(p.B * p.Hkv, p.nsplit), dim3(kWavesF32 * 64), 0, s, p);
   }
@@ -690,21 +802,50 @@ int decode_num_splits(int B, int max_L, int Hkv) {
   return static_cast<int>(ns);
 }
 
-size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D) {
-  const int ns = decode_num_splits(B, max_L, Hkv);
-  const size_t tab = align_up(static_cast<size_t>(max_L) * (D / 2) * sizeof(float2), 256);
-  const size_t tab16 = align_up(static_cast<size_t>(max_L) * D * sizeof(_Float16), 256);
-  const size_t part = static_cast<size_t>(B) * Hq * ns * kWaves * (D + 2) * sizeof(float);  // slots <= kWaves
-  return tab + tab16 + align_up(part, 256);
+// KV heads per bf16 split workgroup: the largest power of two dividing Hkv,
+// at most 8; each head then has 8 / hw wavefronts (partial-state slots).
+static int split_waves_per_head(int Hkv) {
+  int hw = 1;
+  while (hw < kWaves && Hkv % (hw * 2) == 0) hw *= 2;
+  return kWaves / hw;
 }
+
+size_t decode_part_bytes(bool bf16, int B, int max_L, int Hq, int Hkv, int D) {
+  const int ns = decode_num_splits(B, max_L, Hkv);
+  const int slots = bf16 ? split_waves_per_head(Hkv) : kWavesF32;
+  return align_up(static_cast<size_t>(B) * Hq * ns * slots * (D + 2) * sizeof(float), 256);
+}
+
+size_t rope_table_bytes(int npos, int D) {
+  return align_up(static_cast<size_t>(npos) * (D / 2) * sizeof(float2), 256) +
+         align_up(static_cast<size_t>(npos) * D * sizeof(_Float16), 256);
+}
+
+size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D) {
+  const size_t part = std::max(decode_part_bytes(true, B, max_L, Hq, Hkv, D),
+                               decode_part_bytes(false, B, max_L, Hq, Hkv, D));
+  return rope_table_bytes(max_L, D) + part;
+}
+
+hipError_t launch_rope_table_full(void* table, int npos, int D, double theta, hipStream_t s) {
+  const size_t tab = align_up(static_cast<size_t>(npos) * (D / 2) * sizeof(float2), 256);
+  return launch_rope_table(static_cast<float2*>(table), npos, D, theta, s,
+                           reinterpret_cast<uint16_t*>(static_cast<char*>(table) + tab));
+}
+
+bool decode_is_plain(const DecodeCall& c, bool bf16) { return bf16 && c.prerot && c.w0 >= c.max_L; }
 
 hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   if (c.B == 0) return hipSuccess;
   const int ns = decode_num_splits(c.B, c.max_L, c.Hkv);
+  const bool plain = decode_is_plain(c, bf16);
+  // cos/sin rows: the caller's prepared table (rows 0 .. table_rows-1), or
+  // the front of the workspace, built here
   char* ws = static_cast<char*>(c.ws);
-  const size_t tab = align_up(static_cast<size_t>(c.max_L) * (c.D / 2) * sizeof(float2), 256);
-  const size_t tab16 = align_up(static_cast<size_t>(c.max_L) * c.D * sizeof(_Float16), 256);
-  uint16_t* t16 = reinterpret_cast<uint16_t*>(ws + tab);
+  const int npos = c.table ? c.table_rows : c.max_L;
+  char* tbase = c.table ? static_cast<char*>(const_cast<void*>(c.table)) : ws;
+  const size_t tab = align_up(static_cast<size_t>(npos) * (c.D / 2) * sizeof(float2), 256);
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(tbase + tab);
   Params p{};
   p.q = c.q;
   p.kc = c.kc;
@@ -712,9 +853,9 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.sb = c.sb;
   p.ss = c.ss;
   p.sh = c.sh;
-  p.part = reinterpret_cast<float*>(ws + tab + tab16);
+  p.part = c.part ? c.part : reinterpret_cast<float*>(ws + (c.table ? 0 : rope_table_bytes(c.max_L, c.D)));
   p.seq_L = c.seq_L;
-  p.tab = reinterpret_cast<const float2*>(ws);
+  p.tab = reinterpret_cast<const float2*>(tbase);
   p.tab16 = reinterpret_cast<const _Float16*>(t16);
   p.B = c.B;
   p.Hq = c.Hq;
@@ -723,24 +864,24 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.nsplit = ns;
   p.kps = keys_per_split(c.max_L, ns);
   p.max_L = c.max_L;
-  {
-    int hw = 1;  // KV heads per bf16 workgroup: largest power of two dividing Hkv, at most 8
-    while (hw < kWaves && c.Hkv % (hw * 2) == 0) hw *= 2;
-    p.wph = kWaves / hw;
-  }
+  p.wph = split_waves_per_head(c.Hkv);
   p.slots = bf16 ? p.wph : kWavesF32;
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
   p.prerot = c.prerot ? 1 : 0;
-  // rows a decode reads: remote positions (all below w_pretrained) and each
-  // sequence's local window; a pre-rotated cache reads row 0 and the
-  // correction rows j - f(j), which cover the whole range
-  uint16_t* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
-  hipError_t e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s, t16w)
-                          : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B,
-                                                   c.w0, c.w_pretrained, s, t16w);
-  if (e != hipSuccess) return e;
+  p.plain = plain ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (!c.table && !plain) {
+    // rows a decode reads: remote positions (all below w_pretrained) and each
+    // sequence's local window; a pre-rotated cache reads row 0 and the
+    // correction rows j - f(j), which cover the whole range
+    uint16_t* t16w = bf16 ? t16 : nullptr;  // the half rows feed the bf16 split kernel only
+    e = c.prerot ? launch_rope_table(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, s, t16w)
+                 : launch_rope_table_rows(reinterpret_cast<float2*>(ws), c.max_L, c.D, c.theta, c.seq_L, c.B, c.w0,
+                                          c.w_pretrained, s, t16w);
+    if (e != hipSuccess) return e;
+  }
   const int ratio = c.Hq / c.Hkv;
   if (c.D == 128) launch_split_d<128>(p, ratio, bf16, s);
   else launch_split_d<64>(p, ratio, bf16, s);
@@ -748,11 +889,27 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int nparts = ns * p.slots;
   if (c.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(128), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0,
-                       c.seq_L, c.Hq, c.max_L);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(c.B * c.Hq), dim3(kCombThreads), 0, s, p.part, nparts, c.o, c.lse,
+                       bf16 ? 1 : 0, c.seq_L, c.Hq, c.max_L);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(64), 0, s, p.part, nparts, c.o, c.lse, bf16 ? 1 : 0,
-                       c.seq_L, c.Hq, c.max_L);
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(kCombThreads), 0, s, p.part, nparts, c.o, c.lse,
+                       bf16 ? 1 : 0, c.seq_L, c.Hq, c.max_L);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,
+                                  bool prerot, int32_t* out, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int ns = decode_num_splits(B, max_L, Hkv);
+  const int kps = keys_per_split(max_L, ns);
+  const int wph = split_waves_per_head(Hkv);
+  const int threads = ns * wph * 16;
+  const dim3 grid((threads + 255) / 256, B);
+  if (prerot)
+    hipLaunchKernelGGL(key_rows_kernel<true>, grid, dim3(256), 0, s, seq_L, max_L, ns, kps, wph, w_pretrained, w0, out);
+  else
+    hipLaunchKernelGGL(key_rows_kernel<false>, grid, dim3(256), 0, s, seq_L, max_L, ns, kps, wph, w_pretrained, w0,
+                       out);
   return hipGetLastError();
 }
 

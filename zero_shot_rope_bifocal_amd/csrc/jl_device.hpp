@@ -45,6 +45,20 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// x rounded to IEEE half (nearest even), or NaN where x lies outside half
+// range (|x| >= 65520 would round to infinity).  An operand the matrix cores
+// cannot represent then poisons every result that uses it instead of
+// turning it into a wrong finite value.
+__device__ __forceinline__ _Float16 half_or_nan(float x) {
+  return fabsf(x) < 65520.f ? static_cast<_Float16>(x) : static_cast<_Float16>(__builtin_nanf(""));
+}
+
+// Two floats -> packed half_or_nan.
+__device__ __forceinline__ uint32_t pack_f16x2_or_nan(float lo, float hi) {
+  const f16x2 h = {half_or_nan(lo), half_or_nan(hi)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // ---------------------------------------------------------------- rotations
 
 // Table row and sign of sin for rotating a vector that sits at position p to

@@ -39,12 +39,24 @@ struct DecodeCall {
   float scale;
   void* ws;
   bool prerot;  // q and the key cache arrive rotated at their true positions
+  const void* table;  // prepared cos/sin table (rope_table_bytes layout) or null: built in ws
+  int table_rows;     // positions the prepared table covers
+  float* part;        // partial states, or null: in ws after the table
 };
 
 // Workspace layouts (bytes).
 size_t prefill_ws_bytes_bf16(int B, int total_k, int max_k, int Hkv, int D);
 size_t prefill_ws_bytes_f32(int max_k, int D);
 size_t decode_ws_bytes(int B, int max_L, int Hq, int Hkv, int D);
+// Partial states of one decode call (what a prepared-table decode needs).
+size_t decode_part_bytes(bool bf16, int B, int max_L, int Hq, int Hkv, int D);
+// A full cos/sin table of positions [0, npos): fp32 rows [npos][D/2] float2,
+// then (256-byte aligned) the half rows [npos][D] of the decode key rotation.
+size_t rope_table_bytes(int npos, int D);
+hipError_t launch_rope_table_full(void* table, int npos, int D, double theta, hipStream_t s);
+// The signed table rows the bf16 split kernel rotates keys with, [B][max_L].
+hipError_t launch_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,
+                                  bool prerot, int32_t* out, hipStream_t s);
 int decode_num_splits(int B, int max_L, int Hkv);
 
 // Query-block height / key-tile width of the bf16 prefill kernel.

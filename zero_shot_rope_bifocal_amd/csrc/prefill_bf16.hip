@@ -20,7 +20,9 @@
 //  half, accumulation is fp32.  bf16 inputs convert to half exactly (within
 //  +-65504), and rotation keeps each pair's norm, while a rotated value
 //  rounded back to bf16 would carry 8x the rounding error of half (8 vs 11
-//  significant bits) at the same MFMA rate.
+//  significant bits) at the same MFMA rate.  A rotated key, value or scaled
+//  query that half cannot hold is stored as NaN, so the rows that use it
+//  come out NaN rather than finite and wrong.
 //  2. attention: one workgroup = 8 wavefronts = one KV head x HPW query heads
 //     x (32 * 8 / HPW) query positions.  S^T = K Q^T runs on
 //     v_mfma_f32_32x32x16_f16 with the rotated key tile (LDS) as A and the
@@ -139,10 +141,10 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(Params p) {
         r1[hh] = x1 * cr.x - x2 * cr.y;
         r2[hh] = x2 * cr.x + x1 * cr.y;
       }
-      la[e2] = pack_f16x2(l1[0], l1[1]);
-      lb[e2] = pack_f16x2(l2[0], l2[1]);
-      ra[e2] = pack_f16x2(r1[0], r1[1]);
-      rb[e2] = pack_f16x2(r2[0], r2[1]);
+      la[e2] = pack_f16x2_or_nan(l1[0], l1[1]);
+      lb[e2] = pack_f16x2_or_nan(l2[0], l2[1]);
+      ra[e2] = pack_f16x2_or_nan(r1[0], r1[1]);
+      rb[e2] = pack_f16x2_or_nan(r2[0], r2[1]);
     }
     *reinterpret_cast<uint4*>(kl_row + c * 8) = make_uint4(la[0], la[1], la[2], la[3]);
     *reinterpret_cast<uint4*>(kl_row + H + c * 8) = make_uint4(lb[0], lb[1], lb[2], lb[3]);
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float x = bf16_bits_to_float(static_cast<uint16_t>(vv[e >> 1] >> (16 * (e & 1))));
-      vt_col[(c * 16 + e) * 64] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+      vt_col[(c * 16 + e) * 64] = __builtin_bit_cast(uint16_t, half_or_nan(x));
     }
   } else {
     const uint4 z = make_uint4(0, 0, 0, 0);
@@ -306,8 +308,8 @@ __device__ __forceinline__ void rotate_query(f16x8 (&out)[D / 16], const float (
       float2 cs = row[ks * 16 + g * 8 + e];
       cs.y *= rot.sgn;
       const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
-      out[ks][e] = static_cast<_Float16>((x1 * cs.x - x2 * cs.y) * c);
-      out[ks + KS / 2][e] = static_cast<_Float16>((x2 * cs.x + x1 * cs.y) * c);
+      out[ks][e] = half_or_nan((x1 * cs.x - x2 * cs.y) * c);
+      out[ks + KS / 2][e] = half_or_nan((x2 * cs.x + x1 * cs.y) * c);
     }
 }
 

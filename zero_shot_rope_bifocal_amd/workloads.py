@@ -88,6 +88,63 @@ def _normals(seed: int, stream: int, shape, bf16: bool) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normals_range(seed: int, stream: int, start: int, count: int, bf16: bool) -> np.ndarray:
+    """Elements [start, start + count) (row-major order) of the array that
+    ``_normals(seed, stream, shape, bf16)`` returns, drawing only the chunks
+    that hold them."""
+    out = np.empty(count, dtype=np.uint16 if bf16 else np.float32)
+    c0, c1 = start // _CHUNK, (start + count + _CHUNK - 1) // _CHUNK
+    for c in range(c0, c1):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, c))))
+        x = rng.standard_normal(_CHUNK, dtype=np.float32)
+        a, b = max(start, c * _CHUNK), min(start + count, (c + 1) * _CHUNK)
+        out[a - start:b - start] = (_bf16_from_f32(x) if bf16 else x)[a - c * _CHUNK:b - c * _CHUNK]
+    return out
+
+
+def _peak_rows(L0, peaked_rows, peak_seed):
+    return np.sort(np.random.default_rng(peak_seed).choice(L0, peaked_rows, replace=False))
+
+
+def _scale_rows(k, rows, scale, bf16):
+    if bf16:
+        k[rows] = bf16_bits(bits_to_f32(k[rows]) * np.float32(scale))
+    else:
+        k[rows] *= np.float32(scale)
+
+
+def prefill_kv(name: str):
+    """(k, v) of a named one-sequence prefill workload, exactly as
+    ``workload_inputs(name)`` holds them, without drawing the queries."""
+    w = WORKLOADS[name]
+    L, bf16 = w["lens"][0], w["dtype"] == "bf16"
+    k = _normals(w["seed"], 1, (L, w["Hkv"], w["d"]), bf16)
+    v = _normals(w["seed"], 2, (L, w["Hkv"], w["d"]), bf16)
+    if w.get("peaked_rows", 0):
+        _scale_rows(k, _peak_rows(L, w["peaked_rows"], w["peak_seed"]), w["peak_scale"], bf16)
+    return k, v
+
+
+def prefill_q_rows(name: str, row0: int, nrows: int):
+    """Query rows [row0, row0 + nrows) of a named prefill workload."""
+    w = WORKLOADS[name]
+    n = w["Hq"] * w["d"]
+    x = normals_range(w["seed"], 0, row0 * n, nrows * n, w["dtype"] == "bf16")
+    return x.reshape(nrows, w["Hq"], w["d"])
+
+
+def decode_sequence(name: str, b: int):
+    """(q [1, Hq, d], k [1, S, Hkv, d], v [1, S, Hkv, d]) of sequence b of a
+    named decode workload, exactly as ``workload_inputs(name)`` holds them."""
+    w = WORKLOADS[name]
+    bf16 = w["dtype"] == "bf16"
+    nq, nk = w["Hq"] * w["d"], w["L"] * w["Hkv"] * w["d"]
+    q = normals_range(w["seed"], 0, b * nq, nq, bf16).reshape(1, w["Hq"], w["d"])
+    k = normals_range(w["seed"], 1, b * nk, nk, bf16).reshape(1, w["L"], w["Hkv"], w["d"])
+    v = normals_range(w["seed"], 2, b * nk, nk, bf16).reshape(1, w["L"], w["Hkv"], w["d"])
+    return q, k, v
+
+
 def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, peak_scale=1.0,
                    q_lens=None):
     """Packed batch: q [Tq, Hq, d], k/v [Tk, Hkv, d] drawn as streams 0, 1, 2
@@ -106,12 +163,8 @@ def prefill_inputs(lens, Hq, Hkv, d, dtype, seed, peaked_rows=0, peak_seed=0, pe
     v = _normals(seed, 2, (Tk, Hkv, d), bf16)
     peaks = None
     if peaked_rows:
-        peaks = np.sort(np.random.default_rng(peak_seed).choice(lens[0], peaked_rows, replace=False))
-        if bf16:
-            vals = bits_to_f32(k[peaks]) * np.float32(peak_scale)
-            k[peaks] = bf16_bits(vals)
-        else:
-            k[peaks] *= np.float32(peak_scale)
+        peaks = _peak_rows(lens[0], peaked_rows, peak_seed)
+        _scale_rows(k, peaks, peak_scale, bf16)
     cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     return dict(q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k, lens=lens, q_lens=q_lens, peaks=peaks,
