@@ -297,6 +297,27 @@ int jl_bifocal_decode_with_table(const void* q, const void* k_cache, const void*
                                  int table_rows, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned flags);
 
+/* jl_bifocal_decode_with_table for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument, and the call allocates nothing.  The
+ * partial states live in a device array inside the library, one per GPU,
+ * held until the process ends: at most 64 MiB, i.e. B * Hq * splits *
+ * slots * (head_dim + 2) * 4 bytes, the size
+ * jl_bifocal_decode_with_table_workspace_size reports; larger sizes return
+ * JL_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * shares that array, so calls that overlap on one GPU (different streams,
+ * or host threads) race and give wrong results; calls in order on one
+ * stream are safe.  The first call on a device looks up the array's device
+ * address (no allocation); a failure there returns JL_ERR_HIP.  Arguments,
+ * results and flags otherwise as jl_bifocal_decode_with_table. */
+int jl_bifocal_decode_with_table_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                         int64_t stride_b, int64_t stride_s, int64_t stride_h,
+                                         void* o, float* lse, int dtype, const int32_t* seq_L, int B,
+                                         int max_L, int Hq, int Hkv, int head_dim, int w_pretrained,
+                                         int w0, float softmax_scale, const void* table,
+                                         size_t table_bytes, int table_rows, void* stream,
+                                         unsigned flags);
+
 /* Debug export of the bf16 decode's integer map ("Dynamic Bifocal RoPE",
  * eq. G / eq. f): for sequence b (seq_L device int32 [B]) and key j <
  * seq_L[b], rows_out[b * max_L + j] (device int32 [B, max_L]) receives the

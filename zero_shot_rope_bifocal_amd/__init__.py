@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
     L.jl_bifocal_decode_with_table.argtypes = ([c_vp] * 3 + [c_i64] * 3 + [c_vp, c_vp, c_int, c_vp] +
                                                [c_int] * 7 + [c_f, c_vp, c_sz, c_int, c_vp, c_sz, c_vp, c_u])
     L.jl_bifocal_decode_with_table.restype = c_int
+    L.jl_bifocal_decode_with_table_noalloc.argtypes = ([c_vp] * 3 + [c_i64] * 3 + [c_vp, c_vp, c_int, c_vp] +
+                                                       [c_int] * 7 + [c_f, c_vp, c_sz, c_int, c_vp, c_u])
+    L.jl_bifocal_decode_with_table_noalloc.restype = c_int
     L.jl_bifocal_decode_key_rows.argtypes = [c_vp] + [c_int] * 5 + [c_u, c_vp, c_vp]
     L.jl_bifocal_decode_key_rows.restype = c_int
     L.jl_bifocal_remote_positions.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]

@@ -343,6 +343,37 @@ int jl_bifocal_decode_with_table(const void* q, const void* k_cache, const void*
                     "jl_bifocal_decode_with_table launch");
 }
 
+int jl_bifocal_decode_with_table_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                         int64_t stride_b, int64_t stride_s, int64_t stride_h, void* o, float* lse,
+                                         int dtype, const int32_t* seq_L, int B, int max_L, int Hq, int Hkv,
+                                         int head_dim, int w_pretrained, int w0, float softmax_scale,
+                                         const void* table, size_t table_bytes, int table_rows, void* stream,
+                                         unsigned flags) {
+  jl::DecodeCall c;
+  int st = decode_args(q, k_cache, v_cache, stride_b, stride_s, stride_h, o, lse, dtype, seq_L, B, max_L, Hq, Hkv,
+                       head_dim, w_pretrained, w0, 1.0, softmax_scale, flags, &c);
+  if (st != JL_OK || c.B == 0) return st;
+  if (!table) return fail(JL_ERR_INVALID_ARG, "table must be non-null");
+  if (table_rows < max_L) return fail(JL_ERR_INVALID_ARG, "table covers %d positions, max_L = %d", table_rows, max_L);
+  if (table_bytes < jl::rope_table_bytes(table_rows, head_dim))
+    return fail(JL_ERR_INVALID_ARG, "table has %zu bytes, %d rows need %zu", table_bytes, table_rows,
+                jl::rope_table_bytes(table_rows, head_dim));
+  if (reinterpret_cast<uintptr_t>(table) % 256) return fail(JL_ERR_INVALID_ARG, "table must be 256-byte aligned");
+  const size_t need = jl::decode_part_bytes(dtype == JL_BF16, B, max_L, Hq, Hkv, head_dim);
+  if (need > jl::decode_scratch_bytes())
+    return fail(JL_ERR_UNSUPPORTED,
+                "no-allocation decode: these sizes need %zu bytes of partial states, the device scratch holds %zu",
+                need, jl::decode_scratch_bytes());
+  void* scr = nullptr;
+  const hipError_t e = jl::decode_scratch(&scr);
+  if (e != hipSuccess) return hip_status(e, "jl_bifocal_decode_with_table_noalloc scratch lookup");
+  c.table = table;
+  c.table_rows = table_rows;
+  c.part = static_cast<float*>(scr);
+  return hip_status(jl::launch_decode(c, dtype == JL_BF16, static_cast<hipStream_t>(stream)),
+                    "jl_bifocal_decode_with_table_noalloc launch");
+}
+
 int jl_bifocal_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,
                                unsigned flags, int32_t* rows_out, void* stream) {
   if (flags & ~static_cast<unsigned>(JL_FLAG_PREROTATED)) return fail(JL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);

@@ -28,6 +28,7 @@
 //   fp32: the same stream with the products on the VALU (4 wavefronts).
 // Kernel 2 (combine): log-sum-exp merge of the per-wavefront partials.
 #include <algorithm>
+#include <mutex>
 
 #include "jl_device.hpp"
 #include "jl_launch.hpp"
@@ -895,6 +896,39 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(combine_kernel<64>, dim3(c.B * c.Hq), dim3(kCombThreads), 0, s, p.part, nparts, c.o, c.lse,
                        bf16 ? 1 : 0, c.seq_L, c.Hq, c.max_L);
   return hipGetLastError();
+}
+
+// Partial states of jl_bifocal_decode_with_table_noalloc, for callers that
+// cannot allocate: a file-scope device array, one per GPU the library runs on,
+// held until the process ends.  Host code must not use the array's name as a
+// device address; it takes the address hipGetSymbolAddress returns, looked up
+// once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,

@@ -54,6 +54,10 @@ size_t decode_part_bytes(bool bf16, int B, int max_L, int Hq, int Hkv, int D);
 // then (256-byte aligned) the half rows [npos][D] of the decode key rotation.
 size_t rope_table_bytes(int npos, int D);
 hipError_t launch_rope_table_full(void* table, int npos, int D, double theta, hipStream_t s);
+// Device scratch of the no-allocation decode: its size, and this device's
+// address of it (looked up once per device, then cached).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 // The signed table rows the bf16 split kernel rotates keys with, [B][max_L].
 hipError_t launch_decode_key_rows(const int32_t* seq_L, int B, int max_L, int Hkv, int w_pretrained, int w0,
                                   bool prerot, int32_t* out, hipStream_t s);
