@@ -23,8 +23,10 @@
  * Conventions shared by every entry point
  *   Memory:   the caller allocates and frees every buffer (inputs, outputs,
  *             workspace).  Pointers marked "device" must be device memory of
- *             the current HIP device.  The library keeps no device state
- *             between calls and allocates nothing.
+ *             the current HIP device.  The library allocates nothing and
+ *             keeps no device state between calls, with one exception:
+ *             jl_bifocal_decode_with_table_noalloc works in a fixed static
+ *             device array of its own (see there).
  *   Streams:  `stream` is a hipStream_t passed as void* (NULL = the default
  *             stream).  Work is only enqueued; nothing synchronises the host.
  *             The host never reads device arguments such as cu_seqlens.

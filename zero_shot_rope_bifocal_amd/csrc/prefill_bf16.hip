@@ -802,7 +802,10 @@ __global__ __launch_bounds__(64 * 8 / NRB) void attn_kernel(Params p) {
         const int d = mb * 32 + q4 * 8 + g * 4;
         const uint32_t w0v = pack_bf16x2(acc[rb][mb][q4 * 4 + 0] * inv, acc[rb][mb][q4 * 4 + 1] * inv);
         const uint32_t w1v = pack_bf16x2(acc[rb][mb][q4 * 4 + 2] * inv, acc[rb][mb][q4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(dst + d) = make_uint2(w0v, w1v);
+        // non-temporal: O (1 GiB at 128K) is written once and larger than
+        // any cache; left dirty in the caches it is written back in the
+        // middle of whatever kernel runs next
+        __builtin_nontemporal_store(u32x2{w0v, w1v}, reinterpret_cast<u32x2*>(dst + d));
       }
     if (p.lse && g == 0) p.lse[static_cast<int64_t>(h) * p.total_q + tok] = (m_run[rb] + log2f(l_run[rb])) * kLn2;
   }
