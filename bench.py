@@ -374,8 +374,8 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": METRIC,
-        "value": round(pre_tflops, 2),
-        "unit": "TFLOP/s",
+        "value": round(pre_tflops, 2) if do_prefill else round(dec_gbs, 1),
+        "unit": "TFLOP/s" if do_prefill else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -390,10 +390,10 @@ def main():
                         "64 key rows x4) + decode B=16 x L=131072 (same heads)",
             "io_dtype": "bf16",
             "mfma_operands": "f16 (rotated q/k, p, v), fp32 accumulate",
-            "prefill_ms": round(prep_ms + attn_ms, 3),
-            "prefill_prepare_ms": round(prep_ms, 3),
-            "prefill_attend_ms": round(attn_ms, 3),
-            "decode_ms": round(dec_ms, 4),
+            "prefill_ms": round(prep_ms + attn_ms, 3) if do_prefill else None,
+            "prefill_prepare_ms": round(prep_ms, 3) if do_prefill else None,
+            "prefill_attend_ms": round(attn_ms, 3) if do_prefill else None,
+            "decode_ms": round(dec_ms, 4) if do_decode else None,
             "prefill_attend_ms_median_min": [round(median(attn), 3), round(min(attn), 3)] if do_prefill else None,
             "decode_ms_median_min": [round(median(dec), 4), round(min(dec), 4)] if do_decode else None,
             "decode_ms_median_min_50": dec50,
@@ -401,9 +401,9 @@ def main():
             "decode_definition": "one step = jl_bifocal_decode_with_table (split-K kernel + combine) over a cos/sin "
                                  "table of all 131072 positions built once before the timed region; "
                                  "jl_bifocal_decode, which builds the rows it reads on every call, is timed beside it",
-            "decode_GBps": round(dec_gbs, 1),
-            "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
-            "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4),
+            "decode_GBps": round(dec_gbs, 1) if do_decode else None,
+            "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM, 4) if do_decode else None,
+            "prefill_frac_mfma_peak": round(pre_tflops / PEAK_MFMA_16BIT, 4) if do_prefill else None,
             "stages": args.only or "prefill+decode",
             "gpu": props.name,
             "cu_count": props.multi_processor_count,
@@ -417,7 +417,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_MFMA_16BIT, 4),
             "traffic": traffic,
-        },
+        } if do_prefill else None,
         "roofline_decode": {
             "kernel": "decode (split + combine over the prepared table)",
             "bound": "hbm",
@@ -426,7 +426,7 @@ def main():
             "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM, 4),
             "traffic": dtraffic,
-        },
+        } if do_decode else None,
         "cpu_baseline": cpu,
         "plain_rope_baseline": plain,
         "inclusion_exclusion_route": ie,
