@@ -95,8 +95,11 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 // the same in every lane.  Counted by vmcnt like any other load.
 __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  // cache policy 2 = nt: the cache is streamed once per call (the K rows
+  // are loaded non-temporal too), which measured ~2.4% faster than cached
+  // loads at 16 x 128K
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(gsrc),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 2);
 #endif
 }
 
@@ -221,7 +224,10 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   const uint16_t* krow = TAIL ? c.kc + jkr * c.ss + g * 8 : c.klane + j0 * c.ss;
   uint4 kr[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) kr[t] = *reinterpret_cast<const uint4*>(krow + t * 32);
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + t * 32));
+    kr[t] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
 #pragma unroll
   for (int t = 0; t < kKB / RPI; ++t) {
     const uint16_t* src;
