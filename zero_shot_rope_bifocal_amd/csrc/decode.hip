@@ -93,6 +93,8 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 // 16 bytes per lane from global memory straight into LDS (gfx950
 // global_load_lds_dwordx4): lane l writes lds_base + 16*l; lds_base must be
 // the same in every lane.  Counted by vmcnt like any other load.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // cache policy 2 = nt: the cache is streamed once per call (the K rows

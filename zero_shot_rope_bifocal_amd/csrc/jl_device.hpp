@@ -28,7 +28,6 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
 }
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Round to nearest even (gfx950 v_cvt_pk_bf16_f32).
