@@ -68,10 +68,11 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
         pytest.skip("no GPU")
     L = jl.lib()
     vp = ctypes.c_void_p
-    # 64 sequences x 64 heads over 128K keys: 32 splits x 130 floats each > 64 MiB
-    need = jl.decode_with_table_workspace_size(jl.JL_BF16, 64, 131072, 64, 8, 128)
+    # 4096 sequences x 64 heads over 128K keys: at least one partial state of
+    # 130 floats per (sequence, head, wave) > 64 MiB
+    need = jl.decode_with_table_workspace_size(jl.JL_BF16, 4096, 131072, 64, 8, 128)
     assert need > 64 << 20
     rc = L.jl_bifocal_decode_with_table_noalloc(vp(256), vp(256), vp(256), 131072 * 8 * 128, 8 * 128, 128, vp(256),
-                                                None, jl.JL_BF16, vp(256), 64, 131072, 64, 8, 128, 32768, 2048, 0.0,
+                                                None, jl.JL_BF16, vp(256), 4096, 131072, 64, 8, 128, 32768, 2048, 0.0,
                                                 vp(256), 1 << 40, 131072, None, 0)
     assert rc == -2 and b"scratch" in L.jl_last_error()

@@ -795,20 +795,24 @@ int keys_per_split(int max_L, int nsplit) {
 
 }  // namespace
 
-// Key-range splits per (sequence, KV head): about 16384 streaming
-// wavefronts in all (four per slot at the split kernel's 4 waves per SIMD),
-// each split at least 256 keys, and at most 128 splits (the combine merges up
-// to 1024 partial states).
+// Key-range splits per (sequence, KV head).  The bf16 split kernel runs two
+// 8-wavefront workgroups per CU (4 waves per SIMD), i.e. 512 at once on the
+// 256 CUs of gfx950; the grid is sized to fill that once and no more (one
+// round, no tail: at 16 x 128K, 32 splits ran in 1.40 ms against 1.42, 1.45
+// and 1.59 ms for 64, 128 and 256).  Each split keeps at least 256 keys and
+// the combine merges at most 1024 partial states per head.
+constexpr int kResidentSplitGroups = 512;
 int decode_num_splits(int B, int max_L, int Hkv) {
   int hw = 1;
   while (hw < kWaves && Hkv % (hw * 2) == 0) hw *= 2;
-  const int64_t waves = static_cast<int64_t>(B) * Hkv * (kWaves / hw);
-  int64_t ns = (16384 + waves - 1) / waves;
-  const int64_t cap = (static_cast<int64_t>(max_L) + 255) / 256;
-  if (ns > cap) ns = cap;
-  if (ns > 128) ns = 128;
-  if (ns < 1) ns = 1;
-  return static_cast<int>(ns);
+  const int64_t units = static_cast<int64_t>(B) * (Hkv / hw);  // workgroups per split
+  int64_t ns = kResidentSplitGroups / std::max<int64_t>(units, 1);
+  const int64_t cap_keys = (static_cast<int64_t>(max_L) + 255) / 256;
+  // partial states per head: ns * (kWaves / hw) on the bf16 path, ns *
+  // kWavesF32 on the fp32 one
+  const int64_t cap_parts = kMaxParts / std::max(kWaves / hw, kWavesF32);
+  ns = std::min(ns, std::min(cap_keys, cap_parts));
+  return static_cast<int>(std::max<int64_t>(ns, 1));
 }
 
 // KV heads per bf16 split workgroup: the largest power of two dividing Hkv,
@@ -875,6 +879,7 @@ hipError_t launch_decode(const DecodeCall& c, bool bf16, hipStream_t s) {
   p.max_L = c.max_L;
   p.wph = split_waves_per_head(c.Hkv);
   p.slots = bf16 ? p.wph : kWavesF32;
+  if (ns * p.slots > kMaxParts) return hipErrorInvalidValue;  // excluded by decode_num_splits
   p.w_pretrained = c.w_pretrained;
   p.w0 = c.w0;
   p.scale_log2 = c.scale * kLog2e;
