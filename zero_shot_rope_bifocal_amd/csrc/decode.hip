@@ -218,17 +218,26 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   constexpr bool PR = KM == kKeyPre;
   const int col = c.col, g = c.g;
 
-  // ---- K in the A layout (lane = key j0 + col, features t*32 + g*8 ..) and
-  // the V block (row-major, chunk-swizzled) straight into LDS
+  // ---- loads of the block, all issued before the first wait: the cos/sin
+  // rows of the keys' angles (they depend on j only), the V block
+  // (row-major, chunk-swizzled) straight into LDS, and K in the A layout
+  // (lane = key j0 + col, features t*32 + g*8 ..).  Loads into LDS and into
+  // registers share one counter that the compiler cannot split, so the
+  // first use of K waits for all of them: issued together, the block pays
+  // one memory latency instead of one per group.
   const int jk = j0 + col;
   const int jkr = TAIL ? min(jk, c.kend - 1) : jk;
-  // non-tail addresses: a per-lane base plus the wave-uniform row offset
-  const uint16_t* krow = TAIL ? c.kc + jkr * c.ss + g * 8 : c.klane + j0 * c.ss;
-  uint4 kr[NT];
+  RotRow krot{0, 1.f};
+  uint4 cst[HT][2];
+  if constexpr (KM != kKeyPlain) {
+    krot = split_key_rot<PR, TAIL>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
+    const uint4* cs8 =
+        reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(krot.row) * (H / 2) + g * 4) * 4);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + t * 32));
-    kr[t] = make_uint4(x[0], x[1], x[2], x[3]);
+    for (int t = 0; t < HT; ++t) {
+      cst[t][0] = cs8[t * 8];      // frequency pairs e2 = 0, 1
+      cst[t][1] = cs8[t * 8 + 1];  // e2 = 2, 3
+    }
   }
 #pragma unroll
   for (int t = 0; t < kKB / RPI; ++t) {
@@ -242,23 +251,28 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     }
     load_lds16(src, c.vblk + t * 512);
   }
+  // non-tail addresses: a per-lane base plus the wave-uniform row offset
+  const uint16_t* krow = TAIL ? c.kc + jkr * c.ss + g * 8 : c.klane + j0 * c.ss;
+  uint4 kr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + t * 32));
+    kr[t] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   f16x8 a[NT];
   if constexpr (KM != kKeyPlain) {
-  // ---- rotate each key at its own angle (split_key_rot)
-  const RotRow krot = split_key_rot<PR, TAIL>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
-  const int kpos = krot.row;
-  const float ksgn = krot.sgn;
-  // rotation in packed half: the bf16 key converts to half exactly, the half
-  // cos/sin carry at most 2^-12 absolute error, and the result is rounded to
-  // half for the MFMA either way.  A key outside half range turns into
-  // +-inf here, its scores into +-inf or NaN (never finite); NaN and +inf
-  // poison the head's sums by themselves, -inf is caught below.
-  const uint4* cs8 = reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(kpos) * (H / 2) + g * 4) * 4);
-  const f16x2 sgn2 = {static_cast<_Float16>(ksgn), static_cast<_Float16>(ksgn)};
+  // ---- rotate each key at its own angle (split_key_rot) in packed half:
+  // the bf16 key converts to half exactly, the half cos/sin carry at most
+  // 2^-12 absolute error, and the result is rounded to half for the MFMA
+  // either way.  A key outside half range turns into +-inf here, its scores
+  // into +-inf or NaN (never finite); NaN and +inf poison the head's sums by
+  // themselves, -inf is caught below.
+  const f16x2 sgn2 = {static_cast<_Float16>(krot.sgn), static_cast<_Float16>(krot.sgn)};
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    const uint4 ca = cs8[t * 8], cb = cs8[t * 8 + 1];  // frequency pairs e2 = 0, 1 and 2, 3
+    const uint4 ca = cst[t][0], cb = cst[t][1];
     const uint32_t cw[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
