@@ -398,9 +398,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // wavefronts per head: with 8 KV heads every wave streams its own 256-byte
   // slice of the same 2 KB cache rows, and all waves read the same cos/sin rows
   const int hw = kWaves / p.wph;
-  const int hgrp = blockIdx.x % (p.Hkv / hw);
-  const int b = blockIdx.x / (p.Hkv / hw);
-  const int split = blockIdx.y;
+  // workgroup -> (sequence, head group, key range).  Workgroups go to the 8
+  // XCDs in turn (id mod 8); when the ranges divide by 8, XCD x takes ranges
+  // x * ns/8 .. of every sequence, so each XCD's L2 holds the cos/sin rows
+  // of its own eighth of the positions only.
+  const int units = p.B * (p.Hkv / hw);
+  const int id = blockIdx.x;
+  int unit, split;
+  if (p.nsplit % 8 == 0) {
+    const int k = id / 8;
+    unit = k % units;
+    split = (id % 8) * (p.nsplit / 8) + k / units;
+  } else {
+    unit = id % units;
+    split = id / units;
+  }
+  const int hgrp = unit % (p.Hkv / hw);
+  const int b = unit / (p.Hkv / hw);
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = hgrp * hw + wid / p.wph;
@@ -781,7 +795,7 @@ template <int D, int NR>
 void launch_split(const Params& p, bool bf16, hipStream_t s) {
   if (bf16) {
     const int hw = kWaves / p.wph;
-    const dim3 grid(p.B * (p.Hkv / hw), p.nsplit);
+    const dim3 grid(p.B * (p.Hkv / hw) * p.nsplit);
     if (p.plain)
       hipLaunchKernelGGL((split_bf16_kernel<D, NR, kKeyPlain>), grid, dim3(kWaves * 64), 0, s, p);
     else if (p.prerot)
