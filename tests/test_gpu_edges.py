@@ -112,6 +112,26 @@ def test_decode_large_group_size(case):
     check_decode(W.decode_inputs(B, S, Hq, Hkv, d, dt, seed, seq_L=seq_L), wp, w0, theta)
 
 
+# One sequence, so the key ranges are as many as the split rules allow: with
+# one KV head the bf16 kernel runs 8 waves per head and the combine merges
+# its maximum of 1024 partial states; with 8 KV heads, 512 ranges of one wave
+# each (the 128K decode at batch 1); the fp32 kernel at its own slot count.
+MOST_PARTS = [
+    # (B, S, seq_L, Hq, Hkv, d, dtype, wp, w0, theta, seed)
+    (1, 40000, [40000], 4, 1, 128, "bf16", 8192, 2048, 1e6, 91),
+    (1, 40000, [40000], 4, 1, 128, "f32", 8192, 2048, 1e6, 92),
+    (1, 131072, [131072], 32, 8, 128, "bf16", 32768, 2048, 1e6, 93),
+]
+
+
+@pytest.mark.parametrize("case", MOST_PARTS, ids=[f"p{i}" for i in range(len(MOST_PARTS))])
+def test_decode_most_partial_states(case):
+    _torch()
+    B, S, seq_L, Hq, Hkv, d, dt, wp, w0, theta, seed = case
+    _say("decode, most key ranges", case[:3], case[3:])
+    check_decode(W.decode_inputs(B, S, Hq, Hkv, d, dt, seed, seq_L=seq_L), wp, w0, theta)
+
+
 # ---------------------------------------------------------------- window edge
 
 EDGE_PREFILL = [
