@@ -182,7 +182,7 @@ struct SplitCtx {
   int64_t ss;
   int qpos, kend, w0, G, col, g, lane, qcol, nr;
   float invG;
-  int tr_addr[D / 16];  // transposed-read LDS element offsets per 16-feature block
+  int tr_base;  // transposed-read LDS element offset of 16-feature block 0 (block nb: tr_base ^ 16 nb)
 };
 
 // Running state: O block nb in lane (col, g) holds feature nb*16 + col of
@@ -203,12 +203,80 @@ struct SplitState {
 // rotation, Q K^T straight from the stored bf16 keys on the bf16 MFMA.
 enum : int { kKeyRaw = 0, kKeyPre = 1, kKeyPlain = 2 };
 
+// The K rows of one full 16-key block in the A layout (lane = key j0 + col,
+// features t*32 + g*8 ..).  The block walk issues the next block's K rows and
+// V block (by DMA into the wave's other LDS buffer) while the current block
+// is computed; the cos/sin rows (L2 hits) are loaded by each block itself.
+template <int D>
+struct BlockLoads {
+  uint4 kr[D / 32];
+};
+
+// Issues the loads of the full block at j0 from HBM: V into vdst (the wave's
+// LDS buffer for that block), then K, so that waiting for K waits for both.
+template <int D>
+__device__ __forceinline__ void issue_block_loads(const SplitCtx<D>& c, BlockLoads<D>& L, int j0, uint16_t* vdst) {
+  constexpr int NT = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;  // V rows per LDS-load instruction
+#pragma unroll
+  for (int t = 0; t < kKB / RPI; ++t)
+    load_lds16(c.vlane[(t * RPI / 4) & 1] + (j0 + t * RPI) * c.ss, vdst + t * 512);
+  const uint16_t* krow = c.klane + j0 * c.ss;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + t * 32));
+    L.kr[t] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+// The transposing reads of a block's V (one per 16-feature block) in one
+// asm statement that waits for them itself: the compiler would otherwise
+// wait for every outstanding load into LDS (the next block's V) before each
+// of them, since it cannot tell the wave's two V buffers apart.  The caller
+// guarantees that this buffer's loads are complete (they were issued before
+// the K loads the block already waited for).
+__device__ __forceinline__ void lds_read_tr16_all(i16x4 (&o)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_tr16_all(i16x4 (&o)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
 // One 16-key block starting at j0 (wave-uniform).  q0 = j0 / G, r0 = j0 % G.
 // TAIL: the block may run past kend; rows are clamped to kend-1 and their
 // probabilities are zero.
-template <int D, int NR, bool TAIL, int KM>
+// PFM (prefetched, full blocks): the block's loads arrived in L, issued one
+// block earlier; once L's keys and cos/sin rows are consumed (after the
+// rotation; after Q K^T for plain keys) the loads of the block at nj0 go into
+// L when has_next.  Otherwise (the tail, or a walk too short to prefetch)
+// the block issues its own loads and waits for them.
+template <int D, int NR, bool TAIL, int KM, bool PFM = false>
 __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&qrf)[D / 32],
-                                            SplitState<D>& st, int j0, int q0, int r0) {
+                                            SplitState<D>& st, int j0, int q0, int r0,
+                                            BlockLoads<D>* L = nullptr, uint16_t* vcur = nullptr,
+                                            bool has_next = false, int nj0 = 0, int nq0 = 0, int nr0 = 0,
+                                            uint16_t* vnext = nullptr) {
   constexpr int NT = D / 32;
   constexpr int HT = NT / 2;
   constexpr int H = D / 2;
@@ -229,6 +297,22 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   const int jkr = TAIL ? min(jk, c.kend - 1) : jk;
   RotRow krot{0, 1.f};
   uint4 cst[HT][2];
+  uint4 kr[NT];
+  if constexpr (PFM) {
+    static_assert(!TAIL, "the tail block loads for itself");
+    if constexpr (KM != kKeyPlain) {
+      krot = split_key_rot<PR, false>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
+      const uint4* cs8 =
+          reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(krot.row) * (H / 2) + g * 4) * 4);
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+        cst[t][0] = cs8[t * 8];      // frequency pairs e2 = 0, 1
+        cst[t][1] = cs8[t * 8 + 1];  // e2 = 2, 3
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kr[t] = L->kr[t];
+  } else {
   if constexpr (KM != kKeyPlain) {
     krot = split_key_rot<PR, TAIL>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
     const uint4* cs8 =
@@ -253,13 +337,13 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   }
   // non-tail addresses: a per-lane base plus the wave-uniform row offset
   const uint16_t* krow = TAIL ? c.kc + jkr * c.ss + g * 8 : c.klane + j0 * c.ss;
-  uint4 kr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + t * 32));
     kr[t] = make_uint4(x[0], x[1], x[2], x[3]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  }
 
   f16x8 a[NT];
   if constexpr (KM != kKeyPlain) {
@@ -293,6 +377,13 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     }
   }
   }
+  if constexpr (PFM && KM != kKeyPlain) {
+    if (has_next) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_block_loads<D>(c, *L, nj0, vnext);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 
   // ---- S = K_rot Q_sel^T: lane (col = head, g) holds keys j0 + g*4 + rr
   const bool all_remote = c.qpos - (j0 + kKB - 1) >= c.w0;
@@ -304,6 +395,13 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
     for (int t = 0; t < NT; ++t)
       sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[t]), __builtin_bit_cast(bf16x8, qrf[t]),
                                                    sl, 0, 0, 0);
+    if constexpr (PFM) {
+      if (has_next) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_block_loads<D>(c, *L, nj0, vnext);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   } else if (!all_local) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], qrf[t], sr, 0, 0, 0);
@@ -373,11 +471,27 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   // keys; lane (col, g) holds keys g*4 .. g*4+3 of head col, exactly where
   // Q K^T left them), B = V (16 keys x 16 features) from one transposing
   // LDS read
+  if constexpr (PFM) {
+    // the other V buffer is being filled for the next block meanwhile
+    i16x4 bv[NB];
+    uint32_t ad[NB];
+    const uint32_t vb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) const uint16_t*)((__attribute__((address_space(3))) const void*)vcur)));
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const i16x4 bv = lds_read_tr16(c.vblk + c.tr_addr[nb]);
-    st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.o[nb], 0, 0, 0);
-    st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.o[nb], 0, 0, 0);
+    for (int nb = 0; nb < NB; ++nb) ad[nb] = vb + 2u * static_cast<uint32_t>(c.tr_base ^ (nb << 4));
+    lds_read_tr16_all(bv, ad);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv[nb], st.o[nb], 0, 0, 0);
+      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv[nb], st.o[nb], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const i16x4 bv = lds_read_tr16(c.vblk + (c.tr_base ^ (nb << 4)));
+      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.o[nb], 0, 0, 0);
+      st.o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.o[nb], 0, 0, 0);
+    }
   }
 }
 
@@ -389,7 +503,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int H = D / 2;
   constexpr int NB = D / 16;    // PV MFMAs per 16 keys (16 features each)
   static_assert(NR <= 16, "one MFMA column per query head");
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kWaves][kKB * D];  // per-wave V block
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kWaves][2][kKB * D];  // per-wave V blocks (two buffers)
   // B fragments of the query heads rotated at qpos (needed only by key
   // blocks that reach into the local window): [wave][t][g][head]
   __shared__ f16x8 sQl[kWaves][NT * 4 * NR];
@@ -435,7 +549,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   c.tab = p.tab;
   c.tab16 = p.tab16;
   c.ql = sQl[wid];
-  c.vblk = sV[wid];
+  c.vblk = sV[wid][0];
   c.ss = p.ss;
   c.qpos = qpos;
   c.kend = kend;
@@ -520,8 +634,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     const int tr_half = (col & 1) * 4;
     const int tr_c = (col >> 1) & 1;
     const int tr_x = vswz<D>(tr_row);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) c.tr_addr[nb] = tr_row * D + ((nb * 2 + tr_c) ^ tr_x) * 8 + tr_half;
+    // block nb's chunk is (2 nb + tr_c) ^ tr_x with tr_x even, i.e. 2 (nb ^ tr_x / 2) + tr_c: the
+    // block index enters the element offset as 16 (nb ^ tr_x / 2), on bits no other term uses
+    c.tr_base = tr_row * D + (tr_c * 8 + tr_half) + (tr_x / 2) * 16;
   }
 
   SplitState<D> st;
@@ -531,8 +646,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   st.l = 0.f;
   st.bad = false;
 
+  // full blocks: each one's loads are issued while the previous block is
+  // computed; then the tail block, which loads for itself
   KeyBlocks kb(kbeg, w, p.wph, G);
-  for (; kb.j0 + kKB <= kend; kb.next()) split_block<D, NR, false, KM>(c, qrf, st, kb.j0, kb.q0, kb.r0);
+  if (kb.j0 + kKB <= kend) {
+    BlockLoads<D> L;
+    int buf = 0;
+    issue_block_loads<D>(c, L, kb.j0, sV[wid][0]);
+    for (;;) {
+      KeyBlocks nb = kb;
+      nb.next();
+      const bool has_next = nb.j0 + kKB <= kend;
+      split_block<D, NR, false, KM, true>(c, qrf, st, kb.j0, kb.q0, kb.r0, &L, sV[wid][buf], has_next, nb.j0, nb.q0,
+                                          nb.r0, sV[wid][buf ^ 1]);
+      kb = nb;
+      buf ^= 1;
+      if (!has_next) break;
+    }
+  }
   if (kb.j0 < kend) split_block<D, NR, true, KM>(c, qrf, st, kb.j0, kb.q0, kb.r0);
 
   if (st.bad) st.l = __builtin_nanf("");
