@@ -266,11 +266,12 @@ __device__ __forceinline__ void lds_read_tr16_all(i16x4 (&o)[4], const uint32_t 
 // One 16-key block starting at j0 (wave-uniform).  q0 = j0 / G, r0 = j0 % G.
 // TAIL: the block may run past kend; rows are clamped to kend-1 and their
 // probabilities are zero.
-// PFM (prefetched, full blocks): the block's loads arrived in L, issued one
-// block earlier; once L's keys and cos/sin rows are consumed (after the
-// rotation; after Q K^T for plain keys) the loads of the block at nj0 go into
-// L when has_next.  Otherwise (the tail, or a walk too short to prefetch)
-// the block issues its own loads and waits for them.
+// PFM (prefetched, full blocks): the block's K rows arrived in L and its V
+// block in vcur, both issued one block earlier, and only its cos/sin rows are
+// loaded here; once its keys are consumed (after the rotation; after Q K^T
+// for plain keys) the K rows and V block of the block at nj0 are issued into
+// L and vnext when has_next.  Otherwise (the tail block) the block issues
+// all its own loads and waits for them.
 template <int D, int NR, bool TAIL, int KM, bool PFM = false>
 __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&qrf)[D / 32],
                                             SplitState<D>& st, int j0, int q0, int r0,
