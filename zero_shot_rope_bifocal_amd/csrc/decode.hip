@@ -504,7 +504,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int H = D / 2;
   constexpr int NB = D / 16;    // PV MFMAs per 16 keys (16 features each)
   static_assert(NR <= 16, "one MFMA column per query head");
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kWaves][2][kKB * D];  // per-wave V blocks (two buffers)
+  // per-wave V blocks: two buffers for the prefetching walk; with more than 8
+  // query heads per KV head the local query fragments take the LDS that the
+  // second buffer would (two workgroups per CU must fit in 160 KB), and the
+  // walk loads each block for itself
+  constexpr int NVB = NR <= 8 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kWaves][NVB][kKB * D];
   // B fragments of the query heads rotated at qpos (needed only by key
   // blocks that reach into the local window): [wave][t][g][head]
   __shared__ f16x8 sQl[kWaves][NT * 4 * NR];
@@ -650,7 +655,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // full blocks: each one's loads are issued while the previous block is
   // computed; then the tail block, which loads for itself
   KeyBlocks kb(kbeg, w, p.wph, G);
-  if (kb.j0 + kKB <= kend) {
+  if constexpr (NVB == 1) {
+    for (; kb.j0 + kKB <= kend; kb.next()) split_block<D, NR, false, KM>(c, qrf, st, kb.j0, kb.q0, kb.r0);
+  } else if (kb.j0 + kKB <= kend) {
     BlockLoads<D> L;
     int buf = 0;
     issue_block_loads<D>(c, L, kb.j0, sV[wid][0]);
@@ -659,7 +666,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       nb.next();
       const bool has_next = nb.j0 + kKB <= kend;
       split_block<D, NR, false, KM, true>(c, qrf, st, kb.j0, kb.q0, kb.r0, &L, sV[wid][buf], has_next, nb.j0, nb.q0,
-                                          nb.r0, sV[wid][buf ^ 1]);
+                                          nb.r0, sV[wid][(buf ^ 1) % NVB]);
       kb = nb;
       buf ^= 1;
       if (!has_next) break;
