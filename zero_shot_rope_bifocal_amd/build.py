@@ -26,6 +26,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+    # a kernel that misses the waves-per-SIMD its launch shape is sized for
+    # (registers or LDS) is a build error, not a silent slowdown
+    "-Werror=pass-failed",
 ]
 
 
