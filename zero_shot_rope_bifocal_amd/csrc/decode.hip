@@ -299,21 +299,6 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
   RotRow krot{0, 1.f};
   uint4 cst[HT][2];
   uint4 kr[NT];
-  if constexpr (PFM) {
-    static_assert(!TAIL, "the tail block loads for itself");
-    if constexpr (KM != kKeyPlain) {
-      krot = split_key_rot<PR, false>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
-      const uint4* cs8 =
-          reinterpret_cast<const uint4*>(c.tab16 + (static_cast<int64_t>(krot.row) * (H / 2) + g * 4) * 4);
-#pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        cst[t][0] = cs8[t * 8];      // frequency pairs e2 = 0, 1
-        cst[t][1] = cs8[t * 8 + 1];  // e2 = 2, 3
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) kr[t] = L->kr[t];
-  } else {
   if constexpr (KM != kKeyPlain) {
     krot = split_key_rot<PR, TAIL>(jk, col, q0, r0, c.G, c.invG, c.qpos, c.w0, c.kend);
     const uint4* cs8 =
@@ -324,6 +309,11 @@ __device__ __forceinline__ void split_block(const SplitCtx<D>& c, const f16x8 (&
       cst[t][1] = cs8[t * 8 + 1];  // e2 = 2, 3
     }
   }
+  if constexpr (PFM) {
+    static_assert(!TAIL, "the tail block loads for itself");
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kr[t] = L->kr[t];
+  } else {
 #pragma unroll
   for (int t = 0; t < kKB / RPI; ++t) {
     const uint16_t* src;
