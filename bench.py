@@ -263,11 +263,12 @@ def main():
     db = decode_bytes(wd["B"], wd["L"], wd["Hq"], wd["Hkv"], wd["d"])
     dec_gbs = db / (dec_ms * 1e-3) / 1e9 if do_decode else 0.0
 
+    # the digests cover the kernel sources and the build flags they are compiled with
     digest = source_digest("zero_shot_rope_bifocal_amd/csrc/prefill_bf16.hip",
-                           "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
+                           "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp", "zero_shot_rope_bifocal_amd/build.py")
     traffic = load_traffic("prefill_attn", digest)
     ddigest = source_digest("zero_shot_rope_bifocal_amd/csrc/decode.hip",
-                            "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp")
+                            "zero_shot_rope_bifocal_amd/csrc/jl_device.hpp", "zero_shot_rope_bifocal_amd/build.py")
     dtraffic = load_traffic("decode_split", ddigest)
 
     # plain RoPE causal attention on the same kernels, after the timed region:

@@ -32,6 +32,14 @@ FLAGS = [
 ]
 
 
+# per-source flags: the prefill attention kernel runs ~0.9% faster (121.66 ->
+# 120.60 ms at 128K, alternated twice) with the scheduler's max-ILP strategy;
+# the decode kernel is unchanged by it
+SOURCE_FLAGS = {
+    "prefill_bf16.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -41,7 +49,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
